@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: full-size workload (minutes of host time)")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_host_libs():
+    """The generator and the oracle are plain C; build them once if missing."""
+    import oracle
+    import workloads
+    workloads.build(force=False)
+    oracle.build(force=False)
