@@ -1,0 +1,254 @@
+"""Python binding of libgradagg.so, the MI355X gradient-aggregation library.
+
+Argument marshalling only: every step of the aggregation runs in the HIP
+kernels behind the C ABI declared in include/gradagg.h.  PyTorch supplies the
+device memory (tensors) and the stream (the current HIP stream).  There is no
+fallback: if the library is not built, importing the binding's entry points
+raises.
+
+Terms follow the pages: W workers, a layer list, a chunk size and a keep ratio
+(FireCaffe sec. 6 reduction tree; GradientFlow lazy allreduce, mixed precision
+and coarse-grained sparse communication).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgradagg.so")
+
+GA_OK, GA_ERR_INVALID, GA_ERR_ALIGN, GA_ERR_DEVICE, GA_ERR_UNSUPPORTED = range(5)
+GA_FP32, GA_FP16 = 0, 1
+MAX_WORKERS = 1024
+MAX_CHUNKS = 65536
+
+
+class GAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (status_name(status), msg))
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("P", ctypes.c_int64), ("ld", ctypes.c_int64), ("chunk", ctypes.c_int64),
+                ("n_chunks", ctypes.c_int64), ("W", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("mask_words", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class SGD(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("mu", ctypes.c_float)]
+
+
+_VP = ctypes.c_void_p
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgradagg.so is not built (run __graft_entry__.build() or "
+                               "python gradient_aggregation_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        st = ctypes.c_int
+        L.ga_abi_version.restype = ctypes.c_int32
+        L.ga_status_str.restype = ctypes.c_char_p
+        L.ga_status_str.argtypes = [st]
+        L.ga_last_error.restype = ctypes.c_char_p
+        L.ga_plan_compute_info.restype = st
+        L.ga_plan_compute_info.argtypes = [ctypes.c_int32, ctypes.c_int32, _VP, st, ctypes.c_int64,
+                                           ctypes.c_double, ctypes.POINTER(PlanInfo)]
+        L.ga_plan_create.restype = st
+        L.ga_plan_create.argtypes = [ctypes.c_int32, ctypes.c_int32, _VP, st, ctypes.c_int64, ctypes.c_double,
+                                     ctypes.POINTER(_VP)]
+        L.ga_plan_destroy.restype = None
+        L.ga_plan_destroy.argtypes = [_VP]
+        L.ga_plan_get_info.restype = st
+        L.ga_plan_get_info.argtypes = [_VP, ctypes.POINTER(PlanInfo)]
+        L.ga_bucket_pack.restype = st
+        L.ga_bucket_pack.argtypes = [_VP, _VP, _VP, _VP]
+        L.ga_tree_reduce.restype = st
+        L.ga_tree_reduce.argtypes = [_VP, _VP, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
+        L.ga_chunk_norm.restype = st
+        L.ga_chunk_norm.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_chunk_topk.restype = st
+        L.ga_chunk_topk.argtypes = [_VP, _VP, _VP, _VP, _VP]
+        L.ga_chunk_norm_topk.restype = st
+        L.ga_chunk_norm_topk.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_sparse_gather_reduce.restype = st
+        L.ga_sparse_gather_reduce.argtypes = [_VP, _VP, _VP, ctypes.c_int32, _VP, ctypes.POINTER(SGD), _VP, _VP,
+                                              _VP]
+        L.ga_sgd_momentum_apply.restype = st
+        L.ga_sgd_momentum_apply.argtypes = [ctypes.c_int64, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP]
+        _lib = L
+    return _lib
+
+
+def status_name(s: int) -> str:
+    return lib().ga_status_str(s).decode()
+
+
+def _check(s: int) -> None:
+    if s != GA_OK:
+        raise GAError(s, lib().ga_last_error().decode())
+
+
+def compute_info(W: int, layer_numels: Sequence[int], fp16: bool, chunk: int = 0,
+                 keep_ratio: float = 0.0) -> PlanInfo:
+    """Plan sizes without touching a device."""
+    arr = (ctypes.c_int64 * len(layer_numels))(*[int(n) for n in layer_numels])
+    info = PlanInfo()
+    _check(lib().ga_plan_compute_info(W, len(layer_numels), arr, GA_FP16 if fp16 else GA_FP32, chunk,
+                                      keep_ratio, ctypes.byref(info)))
+    return info
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr() -> int:
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _dev(t, dtype, min_numel: int, name: str):
+    """Address of a contiguous CUDA tensor of `dtype` with at least min_numel elements."""
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < min_numel:
+        raise ValueError("%s has %d elements, needs %d" % (name, t.numel(), min_numel))
+    return t.data_ptr()
+
+
+class Plan:
+    """Sizes and the device layer table for W workers and a layer list.
+
+    layer_numels: element count of every layer, in fusion order.
+    fp16: gradients travel as binary16 (summed in binary32) instead of binary32.
+    chunk: chunk size in elements for the sparse path (0: dense only).
+    keep_ratio: fraction of chunks each worker sends.
+    """
+
+    def __init__(self, W: int, layer_numels: Sequence[int], fp16: bool, chunk: int = 0,
+                 keep_ratio: float = 0.0):
+        torch = _torch()
+        if not torch.cuda.is_available():
+            raise RuntimeError("no GPU: the gradient-aggregation library runs on the GPU only")
+        arr = (ctypes.c_int64 * len(layer_numels))(*[int(n) for n in layer_numels])
+        h = _VP()
+        _check(lib().ga_plan_create(W, len(layer_numels), arr, GA_FP16 if fp16 else GA_FP32, chunk,
+                                    keep_ratio, ctypes.byref(h)))
+        self._h = h
+        info = PlanInfo()
+        _check(lib().ga_plan_get_info(h, ctypes.byref(info)))
+        self.info = info
+        self.W, self.P, self.ld = info.W, info.P, info.ld
+        self.chunk, self.n_chunks, self.k, self.mask_words = info.chunk, info.n_chunks, info.k, info.mask_words
+        self.fp16 = fp16
+        self.layer_numels = [int(n) for n in layer_numels]
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().ga_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- buffers ---------------------------------------------------------
+    @property
+    def grad_dtype(self):
+        torch = _torch()
+        return torch.float16 if self.fp16 else torch.float32
+
+    def empty_bucket(self, device="cuda"):
+        return _torch().zeros((self.W, self.ld), dtype=self.grad_dtype, device=device)
+
+    def empty_residual(self, device="cuda"):
+        return _torch().zeros((self.W, self.ld), dtype=_torch().float32, device=device)
+
+    def empty_keys(self, device="cuda"):
+        return _torch().empty((self.W, self.n_chunks), dtype=_torch().float64, device=device)
+
+    def empty_sel(self, device="cuda"):
+        torch = _torch()
+        return (torch.empty((self.W, max(self.k, 1)), dtype=torch.int32, device=device),
+                torch.zeros((self.W, self.mask_words), dtype=torch.int32, device=device))
+
+    # ---- calls -------------------------------------------------------------
+    def bucket_pack(self, layer_ptrs, bucket) -> None:
+        """layer_ptrs: int64 tensor of W*L device addresses, worker-major."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        _check(lib().ga_bucket_pack(self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+                                    _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"), _stream_ptr()))
+
+    def tree_reduce(self, bucket, grad=None, w=None, v=None, lr: Optional[float] = None,
+                    mu: Optional[float] = None) -> None:
+        torch = _torch()
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_tree_reduce(self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),
+                                    _dev(grad, torch.float32, self.P, "grad"), sgd,
+                                    _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
+                                    _stream_ptr()))
+
+    def chunk_norm(self, bucket, resid, keys, prev_mask=None) -> None:
+        torch = _torch()
+        _check(lib().ga_chunk_norm(self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),
+                                   _dev(resid, torch.float32, self.W * self.ld, "resid"),
+                                   _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+                                   _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
+
+    def chunk_topk(self, keys, sel_idx, sel_mask) -> None:
+        torch = _torch()
+        _check(lib().ga_chunk_topk(self._h, _dev(keys, torch.float64, self.W * self.n_chunks, "keys"),
+                                   _dev(sel_idx, torch.int32, self.W * self.k, "sel_idx"),
+                                   _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
+                                   _stream_ptr()))
+
+    def chunk_norm_topk(self, bucket, resid, keys, sel_idx, sel_mask, prev_mask=None) -> None:
+        torch = _torch()
+        _check(lib().ga_chunk_norm_topk(
+            self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"),
+            _dev(sel_idx, torch.int32, self.W * self.k, "sel_idx"),
+            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
+
+    def sparse_gather_reduce(self, resid, sel_mask, zero_selected: bool = True, grad=None, w=None, v=None,
+                             lr: Optional[float] = None, mu: Optional[float] = None) -> None:
+        torch = _torch()
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_sparse_gather_reduce(
+            self._h, _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), int(bool(zero_selected)),
+            _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
+            _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
+
+
+def sgd_momentum_apply(grad, w, v, lr: float, mu: float) -> None:
+    torch = _torch()
+    P = w.numel()
+    _check(lib().ga_sgd_momentum_apply(P, _dev(grad, torch.float32, P, "grad"), _dev(w, torch.float32, P, "w"),
+                                       _dev(v, torch.float32, P, "v"), ctypes.byref(SGD(lr, mu)), _stream_ptr()))

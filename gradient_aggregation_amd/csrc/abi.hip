@@ -1,0 +1,271 @@
+// C ABI of libgradagg.so: plans, argument validation and launches.
+// The operations are specified in include/gradagg.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+ga_status fail(ga_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ga_status ok() {
+    g_err[0] = 0;
+    return GA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+ga_status device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(GA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Fill a plan's sizes; shared by ga_plan_compute_info and ga_plan_create.
+ga_status compute(int32_t W, int32_t L, const int64_t* numel, ga_dtype dt, int64_t chunk, double rho,
+                  ga_plan_info* info) {
+    if (!info) return fail(GA_ERR_INVALID, "info is NULL");
+    if (W < 1 || W > GA_MAX_WORKERS) return fail(GA_ERR_INVALID, "W=%d outside [1,%d]", W, GA_MAX_WORKERS);
+    if (L < 1) return fail(GA_ERR_INVALID, "n_layers=%d < 1", L);
+    if (!numel) return fail(GA_ERR_INVALID, "layer_numel is NULL");
+    if (dt != GA_FP32 && dt != GA_FP16) return fail(GA_ERR_INVALID, "unknown dtype %d", (int)dt);
+    if (chunk < 0) return fail(GA_ERR_INVALID, "chunk=%lld < 0", (long long)chunk);
+    if (!(rho >= 0.0 && rho <= 1.0)) return fail(GA_ERR_INVALID, "keep_ratio %g outside [0,1]", rho);
+    int64_t P = 0;
+    for (int32_t l = 0; l < L; ++l) {
+        if (numel[l] < 1) return fail(GA_ERR_INVALID, "layer %d has %lld elements", l, (long long)numel[l]);
+        if (numel[l] > ((int64_t)1 << 40) || P > ((int64_t)1 << 40))
+            return fail(GA_ERR_UNSUPPORTED, "layer sizes too large");
+        P += numel[l];
+    }
+    // Per-row element indices and rows stay below 2^31 vectors for the grids.
+    if (P > ((int64_t)1 << 35)) return fail(GA_ERR_UNSUPPORTED, "P=%lld too large", (long long)P);
+    memset(info, 0, sizeof *info);
+    info->P = P;
+    info->ld = (P + 63) / 64 * 64;
+    info->W = W;
+    info->n_layers = L;
+    info->dtype = (int32_t)dt;
+    if (chunk > 0) {
+        if (chunk % 8 != 0)
+            return fail(GA_ERR_UNSUPPORTED, "chunk=%lld is not a multiple of 8 elements", (long long)chunk);
+        const int64_t n_c = (P + chunk - 1) / chunk;
+        if (n_c > GA_MAX_CHUNKS)
+            return fail(GA_ERR_UNSUPPORTED, "%lld chunks exceed %d", (long long)n_c, GA_MAX_CHUNKS);
+        double k = ceil(rho * (double)n_c - 1e-9);
+        if (k < 0) k = 0;
+        if (k > (double)n_c) k = (double)n_c;
+        info->chunk = chunk;
+        info->n_chunks = n_c;
+        info->k = (int32_t)k;
+        info->mask_words = (int32_t)((n_c + 31) / 32);
+    }
+    return ok();
+}
+
+ga_plan_info info_of(const ga::Plan* p) {
+    ga_plan_info i;
+    memset(&i, 0, sizeof i);
+    i.P = p->P;
+    i.ld = p->ld;
+    i.chunk = p->C;
+    i.n_chunks = p->n_c;
+    i.W = p->W;
+    i.n_layers = p->L;
+    i.k = p->k;
+    i.mask_words = p->mw;
+    i.dtype = p->dtype;
+    return i;
+}
+
+const ga::Plan* as_plan(const ga_plan* p) { return reinterpret_cast<const ga::Plan*>(p); }
+
+// The calling thread's current device must be the plan's.
+ga_status check_device(const ga::Plan* p) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "hipGetDevice");
+    if (dev != p->device) return fail(GA_ERR_INVALID, "current device %d is not the plan's device %d", dev, p->device);
+    return GA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ga_abi_version(void) { return GA_ABI_VERSION; }
+
+const char* ga_status_str(ga_status s) {
+    switch (s) {
+        case GA_OK: return "GA_OK";
+        case GA_ERR_INVALID: return "GA_ERR_INVALID";
+        case GA_ERR_ALIGN: return "GA_ERR_ALIGN";
+        case GA_ERR_DEVICE: return "GA_ERR_DEVICE";
+        case GA_ERR_UNSUPPORTED: return "GA_ERR_UNSUPPORTED";
+    }
+    return "GA_ERR_UNKNOWN";
+}
+
+const char* ga_last_error(void) { return g_err; }
+
+ga_status ga_plan_compute_info(int32_t W, int32_t n_layers, const int64_t* layer_numel, ga_dtype grad_dtype,
+                               int64_t chunk, double keep_ratio, ga_plan_info* out) {
+    return compute(W, n_layers, layer_numel, grad_dtype, chunk, keep_ratio, out);
+}
+
+ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel, ga_dtype grad_dtype,
+                         int64_t chunk, double keep_ratio, ga_plan** out) {
+    if (!out) return fail(GA_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    ga_plan_info info;
+    ga_status st = compute(W, n_layers, layer_numel, grad_dtype, chunk, keep_ratio, &info);
+    if (st != GA_OK) return st;
+    ga::Plan* p = new (std::nothrow) ga::Plan();
+    if (!p) return fail(GA_ERR_DEVICE, "out of host memory");
+    p->W = W;
+    p->L = n_layers;
+    p->dtype = (int32_t)grad_dtype;
+    p->k = info.k;
+    p->mw = info.mask_words;
+    p->P = info.P;
+    p->ld = info.ld;
+    p->C = info.chunk;
+    p->n_c = info.n_chunks;
+    p->d_offsets = nullptr;
+    p->h_offsets = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_layers + 1));
+    if (!p->h_offsets) {
+        delete p;
+        return fail(GA_ERR_DEVICE, "out of host memory");
+    }
+    p->h_offsets[0] = 0;
+    for (int32_t l = 0; l < n_layers; ++l) p->h_offsets[l + 1] = p->h_offsets[l] + layer_numel[l];
+    hipError_t e = hipGetDevice(&p->device);
+    if (e == hipSuccess) e = hipMalloc((void**)&p->d_offsets, sizeof(int64_t) * (size_t)(n_layers + 1));
+    if (e == hipSuccess)
+        e = hipMemcpy(p->d_offsets, p->h_offsets, sizeof(int64_t) * (size_t)(n_layers + 1), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (p->d_offsets) (void)hipFree(p->d_offsets);
+        free(p->h_offsets);
+        delete p;
+        return device_status(e, "plan device table");
+    }
+    *out = reinterpret_cast<ga_plan*>(p);
+    return ok();
+}
+
+void ga_plan_destroy(ga_plan* plan) {
+    if (!plan) return;
+    ga::Plan* p = reinterpret_cast<ga::Plan*>(plan);
+    if (p->d_offsets) (void)hipFree(p->d_offsets);
+    free(p->h_offsets);
+    delete p;
+}
+
+ga_status ga_plan_get_info(const ga_plan* plan, ga_plan_info* out) {
+    if (!plan || !out) return fail(GA_ERR_INVALID, "NULL argument");
+    *out = info_of(as_plan(plan));
+    return ok();
+}
+
+ga_status ga_bucket_pack(const ga_plan* plan, const uint64_t* d_layer_ptrs, void* d_bucket, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_bucket) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (!aligned16(d_bucket)) return fail(GA_ERR_ALIGN, "bucket not 16-byte aligned");
+    if (((uintptr_t)d_layer_ptrs & 7u) != 0) return fail(GA_ERR_ALIGN, "layer pointer table not 8-byte aligned");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_pack(*p, d_layer_ptrs, d_bucket, stream), "bucket_pack launch");
+}
+
+ga_status ga_tree_reduce(const ga_plan* plan, const void* d_bucket, float* d_grad, const ga_sgd* sgd, float* d_w,
+                         float* d_v, hipStream_t stream) {
+    if (!plan || !d_bucket) return fail(GA_ERR_INVALID, "NULL argument");
+    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
+    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
+    if (!aligned16(d_bucket) || (d_grad && !aligned16(d_grad)) || (sgd && (!aligned16(d_w) || !aligned16(d_v))))
+        return fail(GA_ERR_ALIGN, "device buffers must be 16-byte aligned");
+    const ga::Plan* p = as_plan(plan);
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_tree(*p, d_bucket, d_grad, sgd, d_w, d_v, stream), "tree_reduce launch");
+}
+
+ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_residual, const uint32_t* d_prev_mask,
+                        double* d_keys, hipStream_t stream) {
+    if (!plan || !d_bucket || !d_residual || !d_keys) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (!aligned16(d_bucket) || !aligned16(d_residual) || ((uintptr_t)d_keys & 7u) ||
+        (d_prev_mask && ((uintptr_t)d_prev_mask & 3u)))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_chunk_norm(*p, d_bucket, d_residual, d_prev_mask, d_keys, stream),
+                         "chunk_norm launch");
+}
+
+ga_status ga_chunk_topk(const ga_plan* plan, const double* d_keys, int32_t* d_sel_idx, uint32_t* d_sel_mask,
+                        hipStream_t stream) {
+    if (!plan || !d_keys || !d_sel_mask) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (p->k > 0 && !d_sel_idx) return fail(GA_ERR_INVALID, "sel_idx is NULL with k > 0");
+    if (((uintptr_t)d_keys & 7u) || ((uintptr_t)d_sel_mask & 3u) || (d_sel_idx && ((uintptr_t)d_sel_idx & 3u)))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_topk(*p, d_keys, d_sel_idx, d_sel_mask, stream), "chunk_topk launch");
+}
+
+ga_status ga_chunk_norm_topk(const ga_plan* plan, const void* d_bucket, float* d_residual,
+                             const uint32_t* d_prev_mask, double* d_keys, int32_t* d_sel_idx, uint32_t* d_sel_mask,
+                             hipStream_t stream) {
+    if (!plan || !d_sel_mask || (as_plan(plan)->k > 0 && !d_sel_idx))
+        return fail(GA_ERR_INVALID, "NULL argument");
+    ga_status st = ga_chunk_norm(plan, d_bucket, d_residual, d_prev_mask, d_keys, stream);
+    if (st != GA_OK) return st;
+    return ga_chunk_topk(plan, d_keys, d_sel_idx, d_sel_mask, stream);
+}
+
+ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const uint32_t* d_sel_mask,
+                                  int32_t zero_selected, float* d_grad, const ga_sgd* sgd, float* d_w, float* d_v,
+                                  hipStream_t stream) {
+    if (!plan || !d_residual || !d_sel_mask) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (!d_grad && !sgd && !zero_selected) return fail(GA_ERR_INVALID, "nothing to do");
+    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
+    if (!aligned16(d_residual) || ((uintptr_t)d_sel_mask & 3u) || (d_grad && !aligned16(d_grad)) ||
+        (sgd && (!aligned16(d_w) || !aligned16(d_v))))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(
+        ga::launch_sparse_gather(*p, d_residual, d_sel_mask, zero_selected, d_grad, sgd, d_w, d_v, stream),
+        "sparse_gather_reduce launch");
+}
+
+ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, float* d_v, const ga_sgd* sgd,
+                                hipStream_t stream) {
+    if (P < 0 || !sgd) return fail(GA_ERR_INVALID, "bad size or NULL sgd");
+    if (P == 0) return ok();
+    if (!d_grad || !d_w || !d_v) return fail(GA_ERR_INVALID, "NULL argument");
+    if (!aligned16(d_grad) || !aligned16(d_w) || !aligned16(d_v))
+        return fail(GA_ERR_ALIGN, "device buffers must be 16-byte aligned");
+    return device_status(ga::launch_sgd(P, d_grad, d_w, d_v, sgd, stream), "sgd launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal declarations shared by the HIP sources of libgradagg.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gradagg.h"
+
+namespace ga {
+
+// 128-bit vector of binary32 and its binary16 counterpart.
+struct alignas(16) f4 { float x, y, z, w; };
+
+struct Plan {
+    int32_t W, L, dtype, k, mw;
+    int64_t P, ld, C, n_c;
+    int device;
+    int64_t* d_offsets;  // [L+1] layer start offsets in the fused row
+    int64_t* h_offsets;  // host copy
+};
+
+// ---- launchers (each returns hipSuccess or the launch error) -------------
+hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd,
+                       float* w, float* v, hipStream_t s);
+hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid,
+                             const uint32_t* prev_mask, double* keys, hipStream_t s);
+hipError_t launch_topk(const Plan& p, const double* keys, int32_t* sel_idx, uint32_t* sel_mask,
+                       hipStream_t s);
+hipError_t launch_sparse_gather(const Plan& p, float* resid, const uint32_t* sel_mask,
+                                int zero_selected, float* grad, const ga_sgd* sgd, float* w,
+                                float* v, hipStream_t s);
+hipError_t launch_sgd(int64_t P, const float* g, float* w, float* v, const ga_sgd* sgd,
+                      hipStream_t s);
+hipError_t launch_pack(const Plan& p, const uint64_t* layer_ptrs, void* bucket, hipStream_t s);
+
+// ---- device helpers ------------------------------------------------------
+
+// Momentum SGD, Caffe form, three binary32 roundings (the library is built
+// with -ffp-contract=off, so no multiply-add is fused).
+__device__ __forceinline__ void sgd_update(float g, float lr, float mu, float& w, float& v) {
+    float a = mu * v;
+    float b = lr * g;
+    v = a + b;
+    w = w - v;
+}
+
+}  // namespace ga

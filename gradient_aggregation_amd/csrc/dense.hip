@@ -1,0 +1,191 @@
+// Dense aggregation: fixed-tree sum over W worker rows, mean, fused momentum SGD.
+//
+// Sources: FireCaffe (paperlayer summary) sec. 6 - allreduce is an elementwise
+// sum of the workers' gradient vectors, taken here in a binary reduction tree;
+// GradientFlow (arXiv abstract) - mixed-precision transport, i.e. binary16
+// leaves summed in binary32.
+//
+// Layout and mapping.  The bucket is [W][ld]; a thread owns E consecutive
+// elements (E*sizeof(T) = 16 bytes, so every leaf is one 128-bit load: 8
+// binary16 or 4 binary32 values) and walks the W rows, so each gradient byte
+// is read exactly once and the tree lives in registers.  Workers are loaded
+// U at a time before they are merged, so U 128-bit loads per thread are in
+// flight.  The mean and the SGD update are applied in the same pass: the
+// kernel's HBM traffic is W*P*sizeof(T) + 16*P bytes (w, v read and written).
+#include "common.h"
+#include "tree.h"
+
+namespace ga {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnrollW = 8;
+
+template <bool FP16>
+struct LeafVec;
+
+template <>
+struct LeafVec<false> {
+    static constexpr int E = 4;
+    using raw = float4;
+    static __device__ __forceinline__ void widen(const raw& r, float (&f)[E]) {
+        f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+    }
+};
+
+template <>
+struct LeafVec<true> {
+    static constexpr int E = 8;
+    using raw = uint4;
+    static __device__ __forceinline__ void widen(const raw& r, float (&f)[E]) {
+        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // binary16 -> binary32 is exact (subnormals included).
+            f[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[j] & 0xffffu));
+            f[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[j] >> 16));
+        }
+    }
+};
+
+template <int E>
+__device__ __forceinline__ void epilogue(const float (&s)[E], int64_t i0, int64_t P, float invW,
+                                         float* __restrict__ grad, bool do_sgd, float lr, float mu,
+                                         float* __restrict__ w, float* __restrict__ v) {
+    float g[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) g[e] = s[e] * invW;
+    if (i0 + E <= P) {
+        if (grad) {
+#pragma unroll
+            for (int e = 0; e < E; e += 4)
+                *reinterpret_cast<float4*>(grad + i0 + e) = make_float4(g[e], g[e + 1], g[e + 2], g[e + 3]);
+        }
+        if (do_sgd) {
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                float4 wv = *reinterpret_cast<const float4*>(w + i0 + e);
+                float4 vv = *reinterpret_cast<const float4*>(v + i0 + e);
+                sgd_update(g[e + 0], lr, mu, wv.x, vv.x);
+                sgd_update(g[e + 1], lr, mu, wv.y, vv.y);
+                sgd_update(g[e + 2], lr, mu, wv.z, vv.z);
+                sgd_update(g[e + 3], lr, mu, wv.w, vv.w);
+                *reinterpret_cast<float4*>(w + i0 + e) = wv;
+                *reinterpret_cast<float4*>(v + i0 + e) = vv;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (i0 + e < P) {
+                if (grad) grad[i0 + e] = g[e];
+                if (do_sgd) {
+                    float wv = w[i0 + e], vv = v[i0 + e];
+                    sgd_update(g[e], lr, mu, wv, vv);
+                    w[i0 + e] = wv;
+                    v[i0 + e] = vv;
+                }
+            }
+        }
+    }
+}
+
+template <int LEV, bool FP16>
+__global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ bucket, int64_t ld,
+                                                   int32_t W, int64_t P, float invW,
+                                                   float* __restrict__ grad, int32_t do_sgd, float lr,
+                                                   float mu, float* __restrict__ w,
+                                                   float* __restrict__ v) {
+    using LV = LeafVec<FP16>;
+    constexpr int E = LV::E;
+    using raw = typename LV::raw;
+    const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * E;
+    if (i0 >= P) return;
+    const int64_t row_bytes = ld * (FP16 ? 2 : 4);
+    const char* base = static_cast<const char*>(bucket) + i0 * (FP16 ? 2 : 4);
+
+    TreeAcc<LEV, E> tree;
+    uint32_t cnt = 0;
+    for (int32_t w0 = 0; w0 < W; w0 += kUnrollW) {
+        raw x[kUnrollW];
+#pragma unroll
+        for (int u = 0; u < kUnrollW; ++u)
+            if (w0 + u < W) x[u] = *reinterpret_cast<const raw*>(base + (int64_t)(w0 + u) * row_bytes);
+#pragma unroll
+        for (int u = 0; u < kUnrollW; ++u) {
+            if (w0 + u < W) {
+                float f[E];
+                LV::widen(x[u], f);
+                tree.push(f, cnt);
+                ++cnt;
+            }
+        }
+    }
+    float s[E];
+    tree.result((uint32_t)W, s);
+    epilogue<E>(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
+}
+
+__global__ __launch_bounds__(kThreads) void k_sgd(int64_t P, const float* __restrict__ g,
+                                                  float* __restrict__ w, float* __restrict__ v,
+                                                  float lr, float mu) {
+    const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (i0 >= P) return;
+    if (i0 + 4 <= P) {
+        float4 gv = *reinterpret_cast<const float4*>(g + i0);
+        float4 wv = *reinterpret_cast<const float4*>(w + i0);
+        float4 vv = *reinterpret_cast<const float4*>(v + i0);
+        sgd_update(gv.x, lr, mu, wv.x, vv.x);
+        sgd_update(gv.y, lr, mu, wv.y, vv.y);
+        sgd_update(gv.z, lr, mu, wv.z, vv.z);
+        sgd_update(gv.w, lr, mu, wv.w, vv.w);
+        *reinterpret_cast<float4*>(w + i0) = wv;
+        *reinterpret_cast<float4*>(v + i0) = vv;
+    } else {
+        for (int64_t i = i0; i < P; ++i) {
+            float wv = w[i], vv = v[i];
+            sgd_update(g[i], lr, mu, wv, vv);
+            w[i] = wv;
+            v[i] = vv;
+        }
+    }
+}
+
+template <int LEV>
+hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
+                         float* v, hipStream_t s) {
+    const int E = p.dtype == GA_FP16 ? 8 : 4;
+    const int64_t threads = (p.P + E - 1) / E;
+    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const float invW = (float)(1.0 / (double)p.W);
+    const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
+    if (p.dtype == GA_FP16)
+        hipLaunchKernelGGL((k_tree<LEV, true>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W,
+                           p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    else
+        hipLaunchKernelGGL((k_tree<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W,
+                           p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
+                       float* v, hipStream_t s) {
+    if (p.P == 0) return hipSuccess;
+    if (p.W < (1 << 5)) return tree_dispatch<5>(p, bucket, grad, sgd, w, v, s);
+    if (p.W < (1 << 8)) return tree_dispatch<8>(p, bucket, grad, sgd, w, v, s);
+    return tree_dispatch<11>(p, bucket, grad, sgd, w, v, s);
+}
+
+hipError_t launch_sgd(int64_t P, const float* g, float* w, float* v, const ga_sgd* sgd,
+                      hipStream_t s) {
+    if (P == 0) return hipSuccess;
+    const int64_t threads = (P + 3) / 4;
+    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_sgd, dim3(blocks), dim3(kThreads), 0, s, P, g, w, v, sgd->lr, sgd->mu);
+    return hipGetLastError();
+}
+
+}  // namespace ga

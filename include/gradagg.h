@@ -1,0 +1,221 @@
+/*
+ * gradagg.h - C ABI of the MI355X gradient-aggregation library (libgradagg.so).
+ *
+ * The library aggregates the weight gradients of W data-parallel workers that
+ * are held as W buffers in one GPU's HBM, and applies the momentum-SGD update
+ * to binary32 master weights.  Sources, cited by page title and section:
+ *
+ *   [FC] "FireCaffe: near-linear acceleration of deep neural network training
+ *        on compute clusters" (paperlayer summary): sec. 4 (every worker holds
+ *        the model and computes local weight gradients, which are aggregated),
+ *        sec. 6 (allreduce = elementwise sum of the workers' |grad W|-long
+ *        vectors; binary reduction tree, branching factor 2, depth log2 p;
+ *        aggregation reproduces single-GPU numerics), FAQ (deterministic for a
+ *        fixed seed and GPU count; Caffe compatibility).
+ *   [GF] "Optimizing Network Performance for Distributed DNN Training on GPU
+ *        Clusters: ImageNet/AlexNet Training in 1.5 Minutes" (arXiv abstract):
+ *        lazy allreduce (fuse many communication operations into one),
+ *        mixed-precision transport, coarse-grained sparse communication (send
+ *        only important gradient chunks).
+ *
+ * Terms.  W = workers, L = layers, P = sum of the layers' element counts,
+ * ld = row stride of a per-worker buffer in elements (P rounded up to 64),
+ * C = chunk size in elements, n_c = ceil(P / C) chunks per worker (the last
+ * one may be shorter; chunks run across layer boundaries), k = chunks kept per
+ * worker, mw = ceil(n_c / 32) mask words per worker.
+ *
+ * Buffers.  A "bucket" is a [W][ld] row-major array of gradients, binary32 or
+ * binary16 (GA_FP16), row w holding worker w's fused gradient in layer order
+ * with no gap between layers; elements P..ld-1 of a row are padding, never
+ * read into a result.  A "residual" is a [W][ld] binary32 array.  Gradient,
+ * weight and velocity vectors are [P] binary32.
+ *
+ * Ownership.  The caller allocates and owns every buffer passed in; all
+ * pointers named d_* are device pointers on the plan's device.  A plan owns
+ * only a small device table of layer offsets, allocated in ga_plan_create and
+ * freed in ga_plan_destroy.  Every call is asynchronous on `stream`, allocates
+ * nothing and does not synchronize.  A plan is immutable after creation and may
+ * be shared by threads and streams.  Host arrays are read before return.
+ *
+ * Errors.  Arguments are validated on the host before any launch: a bad size,
+ * a NULL pointer or a keep ratio outside [0,1] gives GA_ERR_INVALID; a device
+ * pointer that is not 16-byte aligned gives GA_ERR_ALIGN; a failed launch or
+ * runtime call gives GA_ERR_DEVICE; a size beyond a kernel's limit gives
+ * GA_ERR_UNSUPPORTED.  On error nothing is launched (except GA_ERR_DEVICE,
+ * raised by the launch itself) and ga_last_error() describes it.  A fault
+ * inside a kernel surfaces at the caller's next synchronization.  No C++
+ * exception crosses this interface.
+ *
+ * Determinism.  Every result is a fixed function of the inputs: the summation
+ * order is the fixed tree below, no atomics are used, and repeated calls give
+ * bitwise identical outputs [FC FAQ].
+ */
+#ifndef GRADAGG_H
+#define GRADAGG_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GA_ABI_VERSION 1
+#define GA_MAX_WORKERS 1024
+#define GA_MAX_CHUNKS 65536
+
+typedef enum {
+    GA_OK = 0,
+    GA_ERR_INVALID = 1,
+    GA_ERR_ALIGN = 2,
+    GA_ERR_DEVICE = 3,
+    GA_ERR_UNSUPPORTED = 4
+} ga_status;
+
+typedef enum { GA_FP32 = 0, GA_FP16 = 1 } ga_dtype;
+
+/* Momentum SGD hyper-parameters (Caffe form, see ga_sgd_momentum_apply). */
+typedef struct {
+    float lr;
+    float mu;
+} ga_sgd;
+
+typedef struct {
+    int64_t P;          /* elements per worker */
+    int64_t ld;         /* row stride of buckets and residuals, elements */
+    int64_t chunk;      /* C, 0 for a dense-only plan */
+    int64_t n_chunks;   /* n_c, 0 for a dense-only plan */
+    int32_t W;
+    int32_t n_layers;
+    int32_t k;          /* chunks kept per worker */
+    int32_t mask_words; /* mw */
+    int32_t dtype;      /* ga_dtype of the gradients */
+} ga_plan_info;
+
+typedef struct ga_plan ga_plan;
+
+/* Version of this interface (GA_ABI_VERSION). */
+int32_t ga_abi_version(void);
+
+/* Static name of a status code. */
+const char* ga_status_str(ga_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ga_last_error(void);
+
+/*
+ * Plan arithmetic only (no device access): sizes for W workers and a layer
+ * list (layer_numel[n_layers], host array, every entry >= 1).
+ * chunk = 0 makes a dense-only plan; chunk >= 1 adds the sparse sizes with
+ *   n_c = ceil(P / chunk) and k = min(n_c, ceil(keep_ratio * n_c - 1e-9)),
+ *   i.e. the fewest chunks that are at least the keep ratio of all chunks.
+ * Limits: 1 <= W <= GA_MAX_WORKERS, n_c <= GA_MAX_CHUNKS, 0 <= keep_ratio <= 1.
+ */
+ga_status ga_plan_compute_info(int32_t W, int32_t n_layers, const int64_t* layer_numel,
+                               ga_dtype grad_dtype, int64_t chunk, double keep_ratio,
+                               ga_plan_info* out);
+
+/* Create a plan on the current device (same arguments as above). */
+ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel,
+                         ga_dtype grad_dtype, int64_t chunk, double keep_ratio, ga_plan** out);
+
+/* Destroy a plan (NULL is ignored).  No call using it may still be queued. */
+void ga_plan_destroy(ga_plan* plan);
+
+ga_status ga_plan_get_info(const ga_plan* plan, ga_plan_info* out);
+
+/*
+ * Lazy allreduce fusion [GF]: copy every worker's per-layer gradient tensors
+ * into one flat row of the bucket, in one launch.
+ *   d_layer_ptrs: device array of W*n_layers device addresses, worker-major
+ *                 (entry w*n_layers + l is worker w's layer l, a contiguous
+ *                 tensor of layer_numel[l] elements of the plan's dtype).
+ *                 Tensors need no particular alignment (16-byte aligned ones
+ *                 are copied with 128-bit accesses).
+ *   d_bucket:     [W][ld] output; the padding of each row is set to zero.
+ * The copy is byte-exact: binary16 stays binary16.
+ */
+ga_status ga_bucket_pack(const ga_plan* plan, const uint64_t* d_layer_ptrs, void* d_bucket,
+                         hipStream_t stream);
+
+/*
+ * Dense aggregation [FC sec. 6] with mixed-precision leaves [GF]:
+ *   S[i] = T(0, W) over the workers' elements bucket[w][i], where
+ *     T(lo, 1) = leaf_lo[i]   (binary16 leaves are widened exactly to binary32)
+ *     T(lo, n) = T(lo, h) + T(lo + h, n - h),  h = largest power of two < n,
+ *   i.e. a binary tree that adds adjacent nodes level by level and carries an
+ *   odd last node up; every node is binary32.
+ *   g[i] = S[i] * fl32(1/W)   (each worker reports the mean over its share of
+ *   the batch, so the mean over workers is the single-GPU gradient).
+ * d_grad: [P] output, or NULL not to store g.
+ * sgd: NULL for no update; otherwise d_w and d_v ([P], in/out) receive the
+ *   momentum-SGD update of ga_sgd_momentum_apply with g, fused in the same pass.
+ * At least one of d_grad and sgd must be given.
+ */
+ga_status ga_tree_reduce(const ga_plan* plan, const void* d_bucket, float* d_grad,
+                         const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream);
+
+/*
+ * Coarse-grained sparse communication [GF], part 1 (sparse plan required):
+ * for every worker w and chunk c,
+ *   a[w][i] = fl32(leaf(bucket[w][i]) + r[w][i])  for i in chunk c
+ *   d_residual[w][i] <- a[w][i]
+ *   d_keys[w*n_c + c] = sum over the chunk of (double)a^2   (binary64; each
+ *                       square is exact; summation order is unspecified, so
+ *                       keys agree with the exact sum to ~1e-15 relative)
+ * r is d_residual, except that with d_prev_mask != NULL (lazy-zero mode) the
+ * chunks whose bit is set in d_prev_mask[w][mw] are taken as zero and not read.
+ * Pass the previous step's selection mask there after a gather with
+ * zero_selected = 0.  d_residual must be all zero before the first step.
+ */
+ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_residual,
+                        const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream);
+
+/*
+ * Part 2: per worker, select the k most important chunks by key (the squared
+ * L2 norm orders chunks as the norm does): larger key first, a NaN key above
+ * all others, equal keys by lower chunk index.
+ *   d_sel_idx:  [W][k] selected chunk indices, ascending within each row
+ *               (may be NULL when k == 0).
+ *   d_sel_mask: [W][mw] bitmaps, bit (c & 31) of word c >> 5 set iff chosen;
+ *               bits at or above n_c are zero.
+ */
+ga_status ga_chunk_topk(const ga_plan* plan, const double* d_keys, int32_t* d_sel_idx,
+                        uint32_t* d_sel_mask, hipStream_t stream);
+
+/* ga_chunk_norm followed by ga_chunk_topk on the same stream. */
+ga_status ga_chunk_norm_topk(const ga_plan* plan, const void* d_bucket, float* d_residual,
+                             const uint32_t* d_prev_mask, double* d_keys, int32_t* d_sel_idx,
+                             uint32_t* d_sel_mask, hipStream_t stream);
+
+/*
+ * Part 3: sum what the workers send.  Worker w sends t[w][i] = a[w][i] on its
+ * selected chunks and nothing elsewhere; absent values enter the same fixed
+ * tree as +0 (binary32 throughout, so residual + sent == a exactly):
+ *   S[i] = T(0, W) over t[.][i];   g[i] = S[i] * fl32(1/W).
+ * d_residual holds a (from ga_chunk_norm).  zero_selected != 0 sets the sent
+ * chunks of d_residual to zero, leaving exactly the residual for the next
+ * step; zero_selected == 0 leaves them (lazy-zero mode: pass d_sel_mask as
+ * d_prev_mask of the next ga_chunk_norm; the residual is then d_residual with
+ * the masked chunks read as zero).
+ * d_grad, sgd, d_w, d_v: as in ga_tree_reduce.
+ */
+ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const uint32_t* d_sel_mask,
+                                  int32_t zero_selected, float* d_grad, const ga_sgd* sgd,
+                                  float* d_w, float* d_v, hipStream_t stream);
+
+/*
+ * Momentum SGD on binary32 master weights, Caffe form (FireCaffe runs Caffe
+ * models and reproduces Caffe's numbers [FC FAQ]), per element:
+ *   v <- fl(fl(mu * v) + fl(lr * g));   w <- fl(w - v)
+ * three roundings, no fused multiply-add, no weight decay.  P >= 0 elements.
+ */
+ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, float* d_v,
+                                const ga_sgd* sgd, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRADAGG_H */

@@ -1,0 +1,106 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times, against the oracle run on the host cores.
+
+NiN-, GoogLeNet- and AlexNet-shaped dense aggregation are compared on every
+element.  The AlexNet-shaped W=128 sparse workload (3 consecutive steps,
+lazy-zero residual mode as benchmarked) is compared on every selected index,
+every key, every mean-gradient/weight/velocity element and the residual of a
+sample of workers."""
+import os
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import KEY_RTOL, TOL_FP16_PATH, TOL_FP32, assert_close, assert_same_bits, host, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ga():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gradient_aggregation_amd as ga
+    return ga
+
+
+def log(msg):
+    print("[fullsize] %s" % msg, flush=True)
+
+
+@pytest.mark.parametrize("name", ["nin", "googlenet", "alexnet16"])
+def test_dense_full_size(ga, name):
+    wl = workloads.WORKLOADS[name]
+    plan = ga.Plan(wl.W, wl.numels, wl.fp16)
+    w_ref = workloads.weights(wl)
+    v_ref = np.zeros(wl.P, np.float32)
+    wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
+    gd = torch.empty(wl.P, dtype=torch.float32, device="cuda")
+    for step in (1, 2):
+        t0 = time.time()
+        b = workloads.grad_bucket(wl, step, plan.ld)
+        bd = to_dev(b, wl.fp16)
+        g_ref = oracle.dense_step(b, wl.P, wl.fp16, wl.lr, wl.mu, w_ref, v_ref)
+        del b
+        plan.tree_reduce(bd, gd, wd, vd, wl.lr, wl.mu)
+        torch.cuda.synchronize()
+        del bd
+        assert_close(host(gd), g_ref, TOL_FP16_PATH if wl.fp16 else TOL_FP32, "gbar")
+        assert_same_bits(host(gd), g_ref, "gbar")
+        assert_same_bits(host(wd), w_ref, "w")
+        assert_same_bits(host(vd), v_ref, "v")
+        log("%s step %d ok in %.1fs" % (name, step, time.time() - t0))
+
+
+def test_sparse_alexnet128_full_size(ga):
+    wl = workloads.WORKLOADS["alexnet128_sparse"]
+    C = wl.chunk
+    plan = ga.Plan(wl.W, wl.numels, True, chunk=C, keep_ratio=wl.rho)
+    P, ld, k, n_c = wl.P, plan.ld, plan.k, plan.n_chunks
+    assert (n_c, k) == (1861, 187)
+    seg = workloads.segments(wl)
+    w_ref = workloads.weights(wl)
+    v_ref = np.zeros(P, np.float32)
+    r_ref = np.zeros((wl.W, ld), np.float32)
+    wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
+    rd = plan.empty_residual()
+    keys = plan.empty_keys()
+    idx = torch.empty((wl.W, k), dtype=torch.int32, device="cuda")
+    mask = torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda")
+    gd = torch.empty(P, dtype=torch.float32, device="cuda")
+    bd = torch.empty((wl.W, ld), dtype=torch.float16, device="cuda")
+    sample = [0, 1, 63, 127]
+    for step in (1, 2, 3):
+        t0 = time.time()
+        b = workloads.grad_bucket(wl, step, ld, seg=seg)
+        bd.copy_(torch.from_numpy(b.view(np.float16)))
+        log("step %d generated+uploaded in %.1fs" % (step, time.time() - t0))
+        t1 = time.time()
+        res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
+        del b
+        log("step %d oracle in %.1fs" % (step, time.time() - t1))
+        # lazy-zero mode, one mask buffer reused across steps, as benchmarked
+        plan.chunk_norm_topk(bd, rd, keys, idx, mask, mask if step > 1 else None)
+        plan.sparse_gather_reduce(rd, mask, False, gd, wd, vd, wl.lr, wl.mu)
+        torch.cuda.synchronize()
+        assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
+        assert np.array_equal(host(idx), res.sel_idx), "selected chunk indices differ"
+        assert np.array_equal(host(mask).view(np.uint32), res.sel_mask)
+        assert_close(host(keys), res.keys, KEY_RTOL, "keys")
+        assert_same_bits(host(gd), res.gbar, "gbar")
+        assert_close(host(gd), res.gbar, TOL_FP32, "gbar")
+        assert_same_bits(host(wd), w_ref, "w")
+        assert_same_bits(host(vd), v_ref, "v")
+        m = host(mask).view(np.uint32)
+        for w in sample:
+            r = host(rd[w, :P]).copy()
+            for c in range(n_c):
+                if (int(m[w, c >> 5]) >> (c & 31)) & 1:
+                    r[c * C:min((c + 1) * C, P)] = 0.0
+            assert_same_bits(r, r_ref[w, :P], "residual of worker %d" % w)
+        log("step %d compared in %.1fs (total %.1fs)" % (step, time.time() - t1, time.time() - t0))
