@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the gradient-aggregation hot path on one MI355X.
+
+Default workload: AlexNet-shaped, W=128 workers x P=60,965,224 parameters,
+binary16 gradients, coarse-grained sparse communication with 32768-element
+chunks keeping 10% of them per worker (k=187 of 1861), the residual carried in
+lazy-zero mode, and momentum SGD on binary32 master weights.
+
+One step = chunk norms with the residual (k_chunk_norm), top-k chunk selection
+(k_topk), gather-reduce of the selected chunks fused with the mean and the SGD
+update (k_gather), over one batch of gradients already resident in HBM (three
+gradient batches are cycled so that consecutive steps see fresh inputs).
+
+Prints one JSON line:
+  value            algorithmic GB/s of the whole step, B_alg / step time, where
+                   B_alg = W*P*(2 + 4 + 4) + 16*P bytes (binary16 gradient read,
+                   residual read and write, w and v read and write)
+  roofline         the dominant kernel (k_chunk_norm): 10*W*P bytes per launch
+                   over its mean launch time from HIP events on its stream,
+                   against the 8 TB/s HBM peak
+  cpu_baseline     the oracle timed on the host cores on a sample of workers
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "aggregated gradient GB/s and % of HBM peak, W workers × P params"
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="alexnet128_sparse")
+    ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
+    ap.add_argument("--cpu-baseline", dest="cpu_baseline", action="store_true", default=True)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy (one-layer pack) of known size, for counter calibration")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the "
+                                                    "dominant kernel (from rocprofv3 counters); default: "
+                                                    "profiles/traffic_<workload>.json")
+    return ap.parse_args()
+
+
+def host_threads() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def copy_calibration():
+    """A plain copy of 2 GiB through the pack kernel (W=1, one layer)."""
+    import torch
+    import gradient_aggregation_amd as ga
+    n = 1 << 30                              # binary16 elements = 2 GiB
+    plan = ga.Plan(1, [n], True)
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = plan.empty_bucket()
+    ptrs = torch.tensor([src.data_ptr()], dtype=torch.int64, device="cuda")
+    for _ in range(5):
+        plan.bucket_pack(ptrs, dst)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    plan.bucket_pack(ptrs, dst)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * plan.ld, "ms": ms,
+                      "GBps": (2 * n + 2 * plan.ld) / ms / 1e6}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the W workers are simulated as W buffers in one GPU's HBM, "
+              "so --gpus %d is not supported (use --gpus 1)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gradient_aggregation_amd as ga
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    wl = workloads.WORKLOADS[args.workload]
+    sparse = wl.mode == "sparse"
+    plan = ga.Plan(wl.W, wl.numels, wl.fp16, chunk=wl.chunk, keep_ratio=wl.rho)
+    P, ld, W = wl.P, plan.ld, wl.W
+    thr = host_threads()
+    log("workload %s: W=%d P=%d ld=%d fp16=%s chunk=%d k=%d n_c=%d" % (
+        wl.name, W, P, ld, wl.fp16, plan.chunk, plan.k, plan.n_chunks))
+
+    # ---- inputs: generated on the host, made resident in HBM before timing ----
+    t0 = time.time()
+    seg = workloads.segments(wl)
+    nb = max(1, args.batches)
+    gdt = torch.float16 if wl.fp16 else torch.float32
+    buckets = [torch.zeros((W, ld), dtype=gdt, device="cuda") for _ in range(nb)]
+    row = np.empty(P, np.uint16 if wl.fp16 else np.float32)
+    pinned = torch.empty(P, dtype=gdt).pin_memory()
+    # the CPU leg runs the oracle on the first batch, kept on the host
+    host_first = np.zeros((W, ld), row.dtype) if args.cpu_baseline else None
+    for bi in range(nb):
+        for w in range(W):
+            workloads.grad_row(wl, bi + 1, w, seg, out=row, threads=thr)
+            pinned.numpy().view(row.dtype)[:] = row
+            buckets[bi][w, :P].copy_(pinned, non_blocking=False)
+            if bi == 0 and host_first is not None:
+                host_first[w, :P] = row
+        log("gradient batch %d resident (%.1fs)" % (bi + 1, time.time() - t0))
+    w_init = workloads.weights(wl, threads=thr)
+    wd = torch.from_numpy(w_init).cuda()
+    vd = torch.zeros(P, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    stream = torch.cuda.current_stream()
+    if sparse:
+        rd = plan.empty_residual()
+        keys = plan.empty_keys()
+        idx = torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda")
+        mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
+        names = ["chunk_norm", "topk", "gather_sgd"]
+    else:
+        names = ["tree_sgd"]
+    n_steps = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_steps)]
+
+    def step(t: int, rec: bool):
+        b = buckets[t % nb]
+        e = ev[t]
+        if rec:
+            e[0].record(stream)
+        if sparse:
+            plan.chunk_norm(b, rd, keys, mask if t > 0 else None)
+            if rec:
+                e[1].record(stream)
+            plan.chunk_topk(keys, idx, mask)
+            if rec:
+                e[2].record(stream)
+            plan.sparse_gather_reduce(rd, mask, False, None, wd, vd, wl.lr, wl.mu)
+            if rec:
+                e[3].record(stream)
+        else:
+            plan.tree_reduce(b, None, wd, vd, wl.lr, wl.mu)
+            if rec:
+                e[1].record(stream)
+
+    for t in range(args.warmup):
+        step(t, True)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for t in range(args.warmup, n_steps):
+        step(t, True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    per_kernel = {}
+    for j, nm in enumerate(names):
+        d = [ev[t][j].elapsed_time(ev[t][j + 1]) for t in range(args.warmup, n_steps)]
+        per_kernel[nm] = {"mean_ms": float(np.mean(d)), "min_ms": float(np.min(d)), "max_ms": float(np.max(d))}
+    log("timed %d steps: %.3f ms/step (wall %.3f ms/step); %s" % (
+        args.steps, ms_step, wall * 1e3 / args.steps,
+        ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
+
+    b_in = 2 if wl.fp16 else 4
+    if sparse:
+        b_alg = W * P * (b_in + 4 + 4) + 16 * P
+        dom, dom_bytes = "chunk_norm", W * P * (b_in + 4 + 4)
+    else:
+        b_alg = W * P * b_in + 16 * P
+        dom, dom_bytes = "tree_sgd", b_alg
+    value = b_alg / (ms_step * 1e-3) / 1e9
+    dom_ms = per_kernel[dom]["mean_ms"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
+                               {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom])
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "W": W, "P": P, "grad_dtype": "f16" if wl.fp16 else "f32",
+            "accumulate": "f32 fixed binary tree", "keys": "f64" if sparse else None,
+            "chunk": plan.chunk or None, "keep_ratio": wl.rho if sparse else None,
+            "k": plan.k if sparse else None, "n_chunks": plan.n_chunks if sparse else None,
+            "residual_mode": "lazy-zero" if sparse else None, "gradient_batches": nb,
+            "parallelism": "1 GPU, W workers as HBM buffers",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "bytes_alg_per_step": b_alg,
+        "grad_elements_per_s": W * P / (ms_step * 1e-3),
+        "grad_input_GBps": round(W * P * b_in / (ms_step * 1e-3) / 1e9, 2),
+        "kernels": per_kernel,
+        "roofline": {
+            "kernel": {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom],
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
+            "traffic_source": None if traffic is None else traffic["summary"],
+            "bytes_per_launch": dom_bytes, "mean_launch_ms": round(dom_ms, 4),
+        },
+        "input_generation_s": round(gen_s, 1),
+    }
+
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, plan, host_first, w_init, thr)
+    print(json.dumps(result), flush=True)
+
+
+def measured_traffic(path, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel's sources changed since it was taken."""
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def cpu_baseline(wl, plan, host_bucket, w_init, thr):
+    """The oracle, as it is, timed on the host cores: one whole step of the
+    workload (all W workers) on the first gradient batch."""
+    import oracle
+    P = wl.P
+    b_in = 2 if wl.fp16 else 4
+    sparse = wl.mode == "sparse"
+    w = w_init.copy()
+    v = np.zeros(P, np.float32)
+    t = time.time()
+    if sparse:
+        r = np.zeros(host_bucket.shape, np.float32)
+        oracle.sparse_step(host_bucket, P, wl.fp16, wl.chunk, plan.k, r, wl.lr, wl.mu, w, v, want_keys=False,
+                           want_gbar=False, threads=thr)
+        del r
+    else:
+        oracle.dense_step(host_bucket, P, wl.fp16, wl.lr, wl.mu, w, v, want_gbar=False, threads=thr)
+    t = time.time() - t
+    b_alg = wl.W * P * ((b_in + 8) if sparse else b_in) + 16 * P
+    log("cpu baseline: oracle step over all %d workers in %.2fs on %d threads" % (wl.W, t, thr))
+    return {"value": round(b_alg / t / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
+            "sample": "one whole %s step of the workload (all %d workers, P=%d), first gradient batch, "
+                      "oracle threads=%d, %.2f s" % (wl.mode, wl.W, P, thr, t)}
+
+
+if __name__ == "__main__":
+    main()

@@ -7,9 +7,9 @@
 //                 registers, then across the wavefront with cross-lane moves,
 //                 then across the 4 wavefronts through LDS.  Traffic per
 //                 element: leaf read, residual read, residual write.
-//   k_topk        one workgroup per worker: every chunk's rank under the order
-//                 (key desc, index asc) is counted against all keys staged in
-//                 LDS; rank < k selects.  Exact integer compares, no sort.
+//   k_topk        one workgroup per worker: radix select of the k-th largest
+//                 key on the keys' bit patterns (exact integer compares), then
+//                 masks and the ascending index list by prefix sums.
 //   k_gather      the fixed tree over the workers' transmitted chunks, mean,
 //                 and fused momentum SGD; a worker that did not select a chunk
 //                 contributes +0 without being read.
@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kNormThreads = 256;
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkTile = 4096;
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 8;
 
@@ -162,54 +161,134 @@ __device__ __forceinline__ uint64_t order_key(double k) {
     return u == 0x8000000000000000ull ? 0ull : u;
 }
 
+// Exclusive prefix sum of one value per thread, in thread order, over a
+// workgroup of kTopkThreads threads.  *total receives the sum of all values.
+// Every thread of the workgroup must call it.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* s_wave, int32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int32_t base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkThreads / 64; ++i) {
+        const int32_t t = s_wave[i];
+        base += i < wave ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + x - v;
+}
+
+// One workgroup per worker.  The k-th largest order key T is found by a
+// most-significant-digit radix select (8 passes of 8 bits, LDS histograms);
+// the selection is then every key above T plus the lowest-index keys equal to
+// T, as many as are still needed.  That is exactly the first k chunks of the
+// order (key desc, index asc).  Masks and the ascending index list follow from
+// two workgroup prefix sums in chunk order.
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const double* __restrict__ keys, int32_t n_c,
                                                        int32_t k, int32_t mw,
                                                        int32_t* __restrict__ sel_idx,
                                                        uint32_t* __restrict__ sel_mask) {
     const int32_t w = blockIdx.x;
-    const double* kw = keys + (int64_t)w * n_c;
-    __shared__ uint64_t tile[kTopkTile];
-    __shared__ uint32_t mask[GA_MAX_CHUNKS / 32];
+    const int tid = threadIdx.x;
+    const double* __restrict__ kw = keys + (int64_t)w * n_c;
+    uint32_t* __restrict__ mrow = sel_mask + (int64_t)w * mw;
+    __shared__ uint32_t hist[256];
+    __shared__ uint64_t s_prefix;
+    __shared__ int32_t s_kk;
+    __shared__ int32_t s_wave[kTopkThreads / 64];
 
-    for (int32_t i = threadIdx.x; i < mw; i += kTopkThreads) mask[i] = 0;
-    const bool one_tile = n_c <= kTopkTile;
-    if (one_tile) {
-        for (int32_t i = threadIdx.x; i < n_c; i += kTopkThreads) tile[i] = order_key(kw[i]);
+    if (k == 0) {  // uniform: nothing is sent
+        for (int32_t i = tid; i < mw; i += kTopkThreads) mrow[i] = 0u;
+        return;
     }
-    __syncthreads();
+    int32_t* __restrict__ irow = sel_idx + (int64_t)w * k;
 
-    // Chunk c (owned by thread c mod 1024) is selected iff fewer than k chunks
-    // precede it in the order.  The loop bounds are uniform, so every thread
-    // reaches every barrier.
-    for (int32_t c0 = 0; c0 < n_c; c0 += kTopkThreads) {
-        const int32_t c = c0 + threadIdx.x;
-        const uint64_t kc = c < n_c ? order_key(kw[c]) : 0;
-        int32_t rank = 0;
-        for (int32_t t0 = 0; t0 < n_c; t0 += kTopkTile) {
-            const int32_t tn = n_c - t0 < kTopkTile ? n_c - t0 : kTopkTile;
-            if (!one_tile) {
-                __syncthreads();
-                for (int32_t i = threadIdx.x; i < tn; i += kTopkThreads) tile[i] = order_key(kw[t0 + i]);
-                __syncthreads();
+    uint64_t prefix = 0, pmask = 0;
+    int32_t kk = k;  // rank of the wanted key among the keys that match prefix
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0u;
+        __syncthreads();
+        for (int32_t c = tid; c < n_c; c += kTopkThreads) {
+            const uint64_t key = order_key(kw[c]);
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // Wavefront 0 finds the digit d holding the kk-th largest key:
+            // lane l owns bins 4l..4l+3; a suffix sum over lanes gives the
+            // count of keys in higher bins, and exactly one lane brackets kk.
+            const int lane = tid;
+            const int32_t h0 = (int32_t)hist[4 * lane], h1 = (int32_t)hist[4 * lane + 1];
+            const int32_t h2 = (int32_t)hist[4 * lane + 2], h3 = (int32_t)hist[4 * lane + 3];
+            const int32_t own = h0 + h1 + h2 + h3;
+            int32_t x = own;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int32_t y = __shfl_down(x, off, 64);
+                if (lane + off < 64) x += y;
             }
-            if (c < n_c) {
-                for (int32_t i = 0; i < tn; ++i) {
-                    const uint64_t ko = tile[i];
-                    rank += (ko > kc) || (ko == kc && t0 + i < c);
+            const int32_t above = x - own;
+            if (above < kk && kk <= x) {
+                int32_t cum = above, d;
+                if (cum + h3 >= kk) {
+                    d = 4 * lane + 3;
+                } else if ((cum += h3) + h2 >= kk) {
+                    d = 4 * lane + 2;
+                } else if ((cum += h2) + h1 >= kk) {
+                    d = 4 * lane + 1;
+                } else {
+                    cum += h1;
+                    d = 4 * lane;
                 }
+                s_prefix = prefix | ((uint64_t)d << shift);
+                s_kk = kk - cum;
             }
         }
-        if (c < n_c && rank < k) atomicOr(&mask[c >> 5], 1u << (c & 31));
+        __syncthreads();
+        prefix = s_prefix;
+        kk = s_kk;
+        pmask |= 0xFFull << shift;
     }
-    __syncthreads();
-    for (int32_t i = threadIdx.x; i < mw; i += kTopkThreads) sel_mask[(int64_t)w * mw + i] = mask[i];
-    // A selected chunk's place in the ascending list = selected chunks below it.
-    for (int32_t c = threadIdx.x; c < n_c; c += kTopkThreads) {
-        if ((mask[c >> 5] >> (c & 31)) & 1u) {
-            int32_t pos = __popc(mask[c >> 5] & ((1u << (c & 31)) - 1u));
-            for (int32_t m = 0; m < (c >> 5); ++m) pos += __popc(mask[m]);
-            sel_idx[(int64_t)w * k + pos] = c;
+    const uint64_t T = prefix;  // k-th largest key; kk keys equal to T are taken
+
+    // Each thread owns a run of q consecutive chunks, q a multiple of 32, so
+    // every mask word has one writer.
+    const int32_t q = 32 * ((n_c + 32 * kTopkThreads - 1) / (32 * kTopkThreads));
+    const int32_t c0 = tid * q;
+    const int32_t c1 = c0 + q < n_c ? c0 + q : n_c;
+    int32_t neq = 0;
+    for (int32_t c = c0; c < c1; ++c) neq += order_key(kw[c]) == T;
+    int32_t total;
+    const int32_t eq_base = block_exclusive_scan(neq, s_wave, &total);
+    int32_t nsel = 0, e = eq_base;
+    for (int32_t c = c0; c < c1; ++c) {
+        const uint64_t key = order_key(kw[c]);
+        nsel += (key > T) || (key == T && e < kk);
+        e += key == T;
+    }
+    int32_t pos = block_exclusive_scan(nsel, s_wave, &total);
+    e = eq_base;
+    for (int32_t cw = c0; cw < c1; cw += 32) {
+        uint32_t m = 0u;
+        for (int32_t b = 0; b < 32 && cw + b < c1; ++b) {
+            const int32_t c = cw + b;
+            const uint64_t key = order_key(kw[c]);
+            const bool sel = (key > T) || (key == T && e < kk);
+            e += key == T;
+            if (sel) {
+                m |= 1u << b;
+                irow[pos++] = c;
+            }
         }
+        mrow[cw >> 5] = m;
     }
 }
 
@@ -217,12 +296,113 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const double* __restrict_
 // k_gather
 // ---------------------------------------------------------------------------
 
-// One thread owns 4 consecutive elements (one 128-bit residual load per
-// worker).  With UNIFORM, C is a multiple of the 256 elements a wavefront
-// covers, so the whole wavefront lies in one chunk and the selection bits are
-// wavefront-uniform: unselected workers are skipped by a scalar branch.
-template <int LEV, bool UNIFORM>
-__global__ __launch_bounds__(kGatherThreads) void k_gather(
+// Mean, optional store of g and the fused SGD update for 4 elements at i0.
+__device__ __forceinline__ void gather_epilogue(const float (&s)[4], int64_t i0, int64_t P, float invW,
+                                                float* __restrict__ grad, bool do_sgd, float lr, float mu,
+                                                float* __restrict__ w, float* __restrict__ v) {
+    float g[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = s[e] * invW;
+    if (i0 + 4 <= P) {
+        if (grad) *reinterpret_cast<float4*>(grad + i0) = make_float4(g[0], g[1], g[2], g[3]);
+        if (do_sgd) {
+            float4 wv = *reinterpret_cast<const float4*>(w + i0);
+            float4 vv = *reinterpret_cast<const float4*>(v + i0);
+            sgd_update(g[0], lr, mu, wv.x, vv.x);
+            sgd_update(g[1], lr, mu, wv.y, vv.y);
+            sgd_update(g[2], lr, mu, wv.z, vv.z);
+            sgd_update(g[3], lr, mu, wv.w, vv.w);
+            *reinterpret_cast<float4*>(w + i0) = wv;
+            *reinterpret_cast<float4*>(v + i0) = vv;
+        }
+    } else {
+        for (int e = 0; e < 4; ++e) {
+            if (i0 + e < P) {
+                if (grad) grad[i0 + e] = g[e];
+                if (do_sgd) {
+                    float wv = w[i0 + e], vv = v[i0 + e];
+                    sgd_update(g[e], lr, mu, wv, vv);
+                    w[i0 + e] = wv;
+                    v[i0 + e] = vv;
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void zero4(float* p, int64_t i0, int64_t P) {
+    if (i0 + 4 <= P) {
+        *reinterpret_cast<float4*>(p) = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+        for (int e = 0; e < 4; ++e)
+            if (i0 + e < P) p[e] = 0.f;
+    }
+}
+
+// Uniform-chunk form: C is a multiple of the 256 elements a wavefront covers
+// (4 per lane), so the wavefront lies in one chunk.  Lane l reads worker
+// (g0 + l)'s mask word for that chunk and a ballot turns the 64 bits into a
+// wavefront-uniform bitmap: unselected workers cost no memory access, and a
+// chunk that no worker selected skips the tree (its sum is +0).
+template <int LEV>
+__global__ __launch_bounds__(kGatherThreads) void k_gather_wave(
+    float* __restrict__ resid, int64_t ld, int32_t W, int64_t P, int64_t C,
+    const uint32_t* __restrict__ sel_mask, int32_t mw, int32_t zero_sel, float invW,
+    float* __restrict__ grad, int32_t do_sgd, float lr, float mu, float* __restrict__ w,
+    float* __restrict__ v) {
+    constexpr int E = 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base =
+        ((int64_t)blockIdx.x * kGatherThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
+    if (wave_base >= P) return;  // whole wavefront past the end
+    const int64_t i0 = wave_base + (int64_t)lane * E;
+    const bool valid = i0 < P;
+    const int32_t c = (int32_t)(wave_base / C);
+    const int32_t cw = c >> 5;
+    const uint32_t cb = 1u << (c & 31);
+
+    bool any = false;
+    for (int32_t g0 = 0; g0 < W; g0 += 64) {
+        const bool bit = (g0 + lane < W) && (sel_mask[(int64_t)(g0 + lane) * mw + cw] & cb);
+        any |= __ballot(bit) != 0ull;
+    }
+    float s[E] = {0.f, 0.f, 0.f, 0.f};
+    if (any) {
+        TreeAcc<LEV, E> tree;
+        uint32_t cnt = 0;
+        for (int32_t g0 = 0; g0 < W; g0 += 64) {
+            const bool bit = (g0 + lane < W) && (sel_mask[(int64_t)(g0 + lane) * mw + cw] & cb);
+            const uint64_t m = __ballot(bit);
+            const int32_t gn = W - g0 < 64 ? W - g0 : 64;
+            for (int32_t u0 = 0; u0 < gn; u0 += kGatherUnroll) {
+                float4 x[kGatherUnroll];
+#pragma unroll
+                for (int u = 0; u < kGatherUnroll; ++u) {
+                    x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (u0 + u < gn && ((m >> (u0 + u)) & 1ull) && valid)
+                        x[u] = *reinterpret_cast<const float4*>(resid + (int64_t)(g0 + u0 + u) * ld + i0);
+                }
+#pragma unroll
+                for (int u = 0; u < kGatherUnroll; ++u) {
+                    if (u0 + u < gn) {
+                        float f[E] = {x[u].x, x[u].y, x[u].z, x[u].w};
+                        tree.push(f, cnt);
+                        ++cnt;
+                        if (zero_sel && ((m >> (u0 + u)) & 1ull) && valid)
+                            zero4(resid + (int64_t)(g0 + u0 + u) * ld + i0, i0, P);
+                    }
+                }
+            }
+        }
+        tree.result((uint32_t)W, s);
+    }
+    if (valid) gather_epilogue(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
+}
+
+// General form: each lane finds its own chunk (C a multiple of 8, so the 4
+// elements of a lane share a chunk) and tests every worker's bit itself.
+template <int LEV>
+__global__ __launch_bounds__(kGatherThreads) void k_gather_lane(
     float* __restrict__ resid, int64_t ld, int32_t W, int64_t P, int64_t C,
     const uint32_t* __restrict__ sel_mask, int32_t mw, int32_t zero_sel, float invW,
     float* __restrict__ grad, int32_t do_sgd, float lr, float mu, float* __restrict__ w,
@@ -230,14 +410,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(
     constexpr int E = 4;
     const int64_t i0 = ((int64_t)blockIdx.x * kGatherThreads + threadIdx.x) * E;
     if (i0 >= P) return;
-    int32_t c;
-    if (UNIFORM) {
-        const int64_t wave_base = ((int64_t)blockIdx.x * kGatherThreads +
-                                   (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
-        c = (int32_t)(wave_base / C);
-    } else {
-        c = (int32_t)(i0 / C);
-    }
+    const int32_t c = (int32_t)(i0 / C);
     const int32_t cw = c >> 5;
     const uint32_t cb = 1u << (c & 31);
 
@@ -261,48 +434,13 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(
                 float f[E] = {x[u].x, x[u].y, x[u].z, x[u].w};
                 tree.push(f, cnt);
                 ++cnt;
-                if (zero_sel && on[u]) {
-                    float* rp = resid + (int64_t)(w0 + u) * ld + i0;
-                    if (i0 + E <= P) {
-                        *reinterpret_cast<float4*>(rp) = make_float4(0.f, 0.f, 0.f, 0.f);
-                    } else {
-                        for (int e = 0; e < E; ++e)
-                            if (i0 + e < P) rp[e] = 0.f;
-                    }
-                }
+                if (zero_sel && on[u]) zero4(resid + (int64_t)(w0 + u) * ld + i0, i0, P);
             }
         }
     }
     float s[E];
     tree.result((uint32_t)W, s);
-    float g[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) g[e] = s[e] * invW;
-    if (i0 + E <= P) {
-        if (grad) *reinterpret_cast<float4*>(grad + i0) = make_float4(g[0], g[1], g[2], g[3]);
-        if (do_sgd) {
-            float4 wv = *reinterpret_cast<const float4*>(w + i0);
-            float4 vv = *reinterpret_cast<const float4*>(v + i0);
-            sgd_update(g[0], lr, mu, wv.x, vv.x);
-            sgd_update(g[1], lr, mu, wv.y, vv.y);
-            sgd_update(g[2], lr, mu, wv.z, vv.z);
-            sgd_update(g[3], lr, mu, wv.w, vv.w);
-            *reinterpret_cast<float4*>(w + i0) = wv;
-            *reinterpret_cast<float4*>(v + i0) = vv;
-        }
-    } else {
-        for (int e = 0; e < E; ++e) {
-            if (i0 + e < P) {
-                if (grad) grad[i0 + e] = g[e];
-                if (do_sgd) {
-                    float wv = w[i0 + e], vv = v[i0 + e];
-                    sgd_update(g[e], lr, mu, wv, vv);
-                    w[i0 + e] = wv;
-                    v[i0 + e] = vv;
-                }
-            }
-        }
-    }
+    gather_epilogue(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
 }
 
 template <int LEV>
@@ -314,10 +452,10 @@ hipError_t gather_dispatch(const Plan& p, float* resid, const uint32_t* sel_mask
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
     const bool uniform = (p.C % 256) == 0;
     if (uniform)
-        hipLaunchKernelGGL((k_gather<LEV, true>), dim3(blocks), dim3(kGatherThreads), 0, s, resid, p.ld,
+        hipLaunchKernelGGL((k_gather_wave<LEV>), dim3(blocks), dim3(kGatherThreads), 0, s, resid, p.ld,
                            p.W, p.P, p.C, sel_mask, p.mw, zero_sel, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
     else
-        hipLaunchKernelGGL((k_gather<LEV, false>), dim3(blocks), dim3(kGatherThreads), 0, s, resid, p.ld,
+        hipLaunchKernelGGL((k_gather_lane<LEV>), dim3(blocks), dim3(kGatherThreads), 0, s, resid, p.ld,
                            p.W, p.P, p.C, sel_mask, p.mw, zero_sel, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
     return hipGetLastError();
 }
