@@ -193,6 +193,8 @@ def main():
         args.steps, ms_step, wall * 1e3 / args.steps,
         ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
 
+    pack = time_pack(plan, wl, buckets[-1], stream, ga)
+
     b_in = 2 if wl.fp16 else 4
     if sparse:
         b_alg = W * P * (b_in + 4 + 4) + 16 * P
@@ -240,12 +242,43 @@ def main():
             "traffic_source": None if traffic is None else traffic["summary"],
             "bytes_per_launch": dom_bytes, "mean_launch_ms": round(dom_ms, 4),
         },
+        "pack": pack,
+        "ms_per_step_with_pack": round(ms_step + pack["mean_ms"], 4),
         "input_generation_s": round(gen_s, 1),
     }
 
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, plan, host_first, w_init, thr)
     print(json.dumps(result), flush=True)
+
+
+def time_pack(plan, wl, src_bucket, stream, ga):
+    """Lazy-allreduce fusion measured on its own: the W*L layer tensors (views
+    into one gradient batch, as a producer with separate per-layer tensors
+    would hold them) are fused into a fresh bucket by ga_bucket_pack."""
+    import torch
+    offs = np.cumsum([0] + wl.numels)
+    esz = src_bucket.element_size()
+    base = src_bucket.data_ptr()
+    ptrs = [base + (w * plan.ld + int(offs[l])) * esz for w in range(wl.W) for l in range(len(wl.numels))]
+    table = torch.tensor(ptrs, dtype=torch.int64, device="cuda")
+    dst = plan.empty_bucket()
+    for _ in range(2):
+        plan.bucket_pack(table, dst)
+    reps = 5
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        plan.bucket_pack(table, dst)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    d = [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+    ok = bool(torch.equal(dst, src_bucket))
+    del dst
+    moved = 2 * wl.W * wl.P * esz
+    return {"kernel": "k_pack", "layers": len(wl.numels), "tensors": wl.W * len(wl.numels),
+            "mean_ms": round(float(np.mean(d)), 4), "GBps": round(moved / (np.mean(d) * 1e-3) / 1e9, 1),
+            "bytes": moved, "matches_source": ok}
 
 
 def measured_traffic(path, kernel):
@@ -260,7 +293,10 @@ def measured_traffic(path, kernel):
         return None
     h = hashlib.sha256()
     for src in rec["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
+        path_src = os.path.join(ROOT, src)
+        if not os.path.exists(path_src):
+            return None
+        with open(path_src, "rb") as f:
             h.update(f.read())
     return rec if h.hexdigest() == rec["sources_sha256"] else None
 

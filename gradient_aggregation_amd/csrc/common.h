@@ -44,4 +44,16 @@ __device__ __forceinline__ void sgd_update(float g, float lr, float mu, float& w
     w = w - v;
 }
 
+// binary16 -> binary32 widening (exact, subnormals included) of 8 packed values.
+__device__ __forceinline__ void widen8(const uint4& r, float (&f)[8]) {
+    const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[j] & 0xffffu));
+        f[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[j] >> 16));
+    }
+}
+
+__device__ __forceinline__ float widen1(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 }  // namespace ga

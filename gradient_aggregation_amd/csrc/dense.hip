@@ -48,15 +48,7 @@ template <>
 struct LeafVec<true> {
     static constexpr int E = 8;
     using raw = uint4;
-    static __device__ __forceinline__ void widen(const raw& r, float (&f)[E]) {
-        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // binary16 -> binary32 is exact (subnormals included).
-            f[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[j] & 0xffffu));
-            f[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[j] >> 16));
-        }
-    }
+    static __device__ __forceinline__ void widen(const raw& r, float (&f)[E]) { widen8(r, f); }
 };
 
 template <int E>
