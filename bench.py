@@ -6,10 +6,12 @@ binary16 gradients, coarse-grained sparse communication with 32768-element
 chunks keeping 10% of them per worker (k=187 of 1861), the residual carried in
 lazy-zero mode, and momentum SGD on binary32 master weights.
 
-One step = chunk norms with the residual (k_chunk_norm), top-k chunk selection
-(k_topk), gather-reduce of the selected chunks fused with the mean and the SGD
-update (k_gather), over one batch of gradients already resident in HBM (three
-gradient batches are cycled so that consecutive steps see fresh inputs).
+One step = lazy-allreduce fusion of the W*16 per-layer gradient tensors read
+with zero copy through the layer table, together with the chunk norms and the
+residual (k_chunk_norm), top-k chunk selection (k_topk), and the gather-reduce
+of the selected chunks fused with the mean and the SGD update (k_gather), over
+one batch of gradients already resident in HBM (three gradient batches are
+cycled so that consecutive steps see fresh inputs).
 
 Prints one JSON line:
   value            algorithmic GB/s of the whole step, B_alg / step time, where
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="alexnet128_sparse")
     ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
+    ap.add_argument("--source", choices=["layers", "bucket"], default="layers",
+                    help="gradients as per-layer tensors fused with zero copy (default) or a packed bucket")
     ap.add_argument("--cpu-baseline", dest="cpu_baseline", action="store_true", default=True)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -115,22 +119,43 @@ def main():
         wl.name, W, P, ld, wl.fp16, plan.chunk, plan.k, plan.n_chunks))
 
     # ---- inputs: generated on the host, made resident in HBM before timing ----
+    # Default: every worker's gradient arrives as its own per-layer tensors (as
+    # a backward pass leaves them) and the step fuses them with zero copy by
+    # reading through the layer table.  --source bucket feeds a pre-packed
+    # [W][ld] bucket instead.
     t0 = time.time()
     seg = workloads.segments(wl)
     nb = max(1, args.batches)
     gdt = torch.float16 if wl.fp16 else torch.float32
-    buckets = [torch.zeros((W, ld), dtype=gdt, device="cuda") for _ in range(nb)]
+    offs = np.cumsum([0] + wl.numels)
+    layers_src = args.source == "layers"
+    sources = []            # per batch: int64 layer table (layers) or [W][ld] bucket
+    keep = []               # the layer tensors, kept alive
     row = np.empty(P, np.uint16 if wl.fp16 else np.float32)
     pinned = torch.empty(P, dtype=gdt).pin_memory()
     # the CPU leg runs the oracle on the first batch, kept on the host
     host_first = np.zeros((W, ld), row.dtype) if args.cpu_baseline else None
     for bi in range(nb):
+        if layers_src:
+            tensors = [[torch.empty(n, dtype=gdt, device="cuda") for n in wl.numels] for _ in range(W)]
+        else:
+            bucket = torch.zeros((W, ld), dtype=gdt, device="cuda")
         for w in range(W):
             workloads.grad_row(wl, bi + 1, w, seg, out=row, threads=thr)
             pinned.numpy().view(row.dtype)[:] = row
-            buckets[bi][w, :P].copy_(pinned, non_blocking=False)
+            if layers_src:
+                for l in range(len(wl.numels)):
+                    tensors[w][l].copy_(pinned[offs[l]:offs[l + 1]], non_blocking=False)
+            else:
+                bucket[w, :P].copy_(pinned, non_blocking=False)
             if bi == 0 and host_first is not None:
                 host_first[w, :P] = row
+        if layers_src:
+            keep.append(tensors)
+            sources.append(torch.tensor([t.data_ptr() for tw in tensors for t in tw], dtype=torch.int64,
+                                        device="cuda"))
+        else:
+            sources.append(bucket)
         log("gradient batch %d resident (%.1fs)" % (bi + 1, time.time() - t0))
     w_init = workloads.weights(wl, threads=thr)
     wd = torch.from_numpy(w_init).cuda()
@@ -151,12 +176,15 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_steps)]
 
     def step(t: int, rec: bool):
-        b = buckets[t % nb]
+        b = sources[t % nb]
         e = ev[t]
         if rec:
             e[0].record(stream)
         if sparse:
-            plan.chunk_norm(b, rd, keys, mask if t > 0 else None)
+            if layers_src:
+                plan.chunk_norm_layers(b, rd, keys, mask if t > 0 else None)
+            else:
+                plan.chunk_norm(b, rd, keys, mask if t > 0 else None)
             if rec:
                 e[1].record(stream)
             plan.chunk_topk(keys, idx, mask)
@@ -166,7 +194,10 @@ def main():
             if rec:
                 e[3].record(stream)
         else:
-            plan.tree_reduce(b, None, wd, vd, wl.lr, wl.mu)
+            if layers_src:
+                plan.tree_reduce_layers(b, None, wd, vd, wl.lr, wl.mu)
+            else:
+                plan.tree_reduce(b, None, wd, vd, wl.lr, wl.mu)
             if rec:
                 e[1].record(stream)
 
@@ -193,7 +224,7 @@ def main():
         args.steps, ms_step, wall * 1e3 / args.steps,
         ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
 
-    pack = time_pack(plan, wl, buckets[-1], stream, ga)
+    pack = time_pack(plan, wl, sources[-1], keep[-1] if layers_src else None, stream)
 
     b_in = 2 if wl.fp16 else 4
     if sparse:
@@ -227,6 +258,8 @@ def main():
             "chunk": plan.chunk or None, "keep_ratio": wl.rho if sparse else None,
             "k": plan.k if sparse else None, "n_chunks": plan.n_chunks if sparse else None,
             "residual_mode": "lazy-zero" if sparse else None, "gradient_batches": nb,
+            "fusion": "zero-copy read of %d per-layer tensors" % (W * len(wl.numels)) if layers_src
+                      else "pre-packed bucket",
             "parallelism": "1 GPU, W workers as HBM buffers",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -252,16 +285,19 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_pack(plan, wl, src_bucket, stream, ga):
-    """Lazy-allreduce fusion measured on its own: the W*L layer tensors (views
-    into one gradient batch, as a producer with separate per-layer tensors
-    would hold them) are fused into a fresh bucket by ga_bucket_pack."""
+def time_pack(plan, wl, src, layer_tensors, stream):
+    """Lazy-allreduce fusion as a copy, measured on its own: the W*L layer
+    tensors of one gradient batch are packed into a fresh bucket by
+    ga_bucket_pack (context for producers that need a materialized bucket)."""
     import torch
     offs = np.cumsum([0] + wl.numels)
-    esz = src_bucket.element_size()
-    base = src_bucket.data_ptr()
-    ptrs = [base + (w * plan.ld + int(offs[l])) * esz for w in range(wl.W) for l in range(len(wl.numels))]
-    table = torch.tensor(ptrs, dtype=torch.int64, device="cuda")
+    if layer_tensors is not None:
+        table = src
+    else:
+        esz = src.element_size()
+        table = torch.tensor([src.data_ptr() + (w * plan.ld + int(offs[l])) * esz
+                              for w in range(wl.W) for l in range(len(wl.numels))], dtype=torch.int64,
+                             device="cuda")
     dst = plan.empty_bucket()
     for _ in range(2):
         plan.bucket_pack(table, dst)
@@ -273,8 +309,12 @@ def time_pack(plan, wl, src_bucket, stream, ga):
         ev[r + 1].record(stream)
     torch.cuda.synchronize()
     d = [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
-    ok = bool(torch.equal(dst, src_bucket))
+    ok = True
+    for w in (0, wl.W - 1):
+        ref = torch.cat(layer_tensors[w]) if layer_tensors is not None else src[w, :wl.P]
+        ok = ok and bool(torch.equal(dst[w, :wl.P], ref))
     del dst
+    esz = 2 if wl.fp16 else 4
     moved = 2 * wl.W * wl.P * esz
     return {"kernel": "k_pack", "layers": len(wl.numels), "tensors": wl.W * len(wl.numels),
             "mean_ms": round(float(np.mean(d)), 4), "GBps": round(moved / (np.mean(d) * 1e-3) / 1e9, 1),

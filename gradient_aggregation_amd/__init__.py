@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.ga_bucket_pack.argtypes = [_VP, _VP, _VP, _VP]
         L.ga_tree_reduce.restype = st
         L.ga_tree_reduce.argtypes = [_VP, _VP, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
+        L.ga_tree_reduce_layers.restype = st
+        L.ga_tree_reduce_layers.argtypes = [_VP, _VP, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
+        L.ga_chunk_norm_layers.restype = st
+        L.ga_chunk_norm_layers.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
         L.ga_chunk_norm.restype = st
         L.ga_chunk_norm.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
         L.ga_chunk_topk.restype = st
@@ -211,6 +215,27 @@ class Plan:
                                     _dev(grad, torch.float32, self.P, "grad"), sgd,
                                     _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
                                     _stream_ptr()))
+
+    def tree_reduce_layers(self, layer_ptrs, grad=None, w=None, v=None, lr: Optional[float] = None,
+                           mu: Optional[float] = None) -> None:
+        """tree_reduce reading the leaves straight from the per-layer tensors
+        (layer_ptrs: int64 tensor of W*L device addresses, worker-major)."""
+        torch = _torch()
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        L = len(self.layer_numels)
+        _check(lib().ga_tree_reduce_layers(self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+                                           _dev(grad, torch.float32, self.P, "grad"), sgd,
+                                           _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
+                                           _stream_ptr()))
+
+    def chunk_norm_layers(self, layer_ptrs, resid, keys, prev_mask=None) -> None:
+        """chunk_norm reading the gradient straight from the per-layer tensors."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        _check(lib().ga_chunk_norm_layers(self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+                                          _dev(resid, torch.float32, self.W * self.ld, "resid"),
+                                          _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+                                          _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
 
     def chunk_norm(self, bucket, resid, keys, prev_mask=None) -> None:
         torch = _torch()

@@ -152,12 +152,37 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
     }
     p->h_offsets[0] = 0;
     for (int32_t l = 0; l < n_layers; ++l) p->h_offsets[l + 1] = p->h_offsets[l] + layer_numel[l];
+    // wavefront-tile -> layer table for the kernels that read the layer tensors
+    const int64_t vec = grad_dtype == GA_FP16 ? 8 : 4;
+    p->tile_elems = 64 * vec;
+    const int64_t n_tiles = (info.P + p->tile_elems - 1) / p->tile_elems;
+    uint32_t* h_tiles = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)n_tiles);
+    if (!h_tiles) {
+        free(p->h_offsets);
+        delete p;
+        return fail(GA_ERR_DEVICE, "out of host memory");
+    }
+    {
+        int32_t l = 0;
+        for (int64_t t = 0; t < n_tiles; ++t) {
+            const int64_t e0 = t * p->tile_elems;
+            while (p->h_offsets[l + 1] <= e0) ++l;
+            const bool whole = p->h_offsets[l + 1] >= e0 + p->tile_elems && p->h_offsets[l] % vec == 0;
+            h_tiles[t] = (uint32_t)l | (whole ? 0x80000000u : 0u);
+        }
+    }
+    p->d_tile_layer = nullptr;
     hipError_t e = hipGetDevice(&p->device);
     if (e == hipSuccess) e = hipMalloc((void**)&p->d_offsets, sizeof(int64_t) * (size_t)(n_layers + 1));
     if (e == hipSuccess)
         e = hipMemcpy(p->d_offsets, p->h_offsets, sizeof(int64_t) * (size_t)(n_layers + 1), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMalloc((void**)&p->d_tile_layer, sizeof(uint32_t) * (size_t)n_tiles);
+    if (e == hipSuccess)
+        e = hipMemcpy(p->d_tile_layer, h_tiles, sizeof(uint32_t) * (size_t)n_tiles, hipMemcpyHostToDevice);
+    free(h_tiles);
     if (e != hipSuccess) {
         if (p->d_offsets) (void)hipFree(p->d_offsets);
+        if (p->d_tile_layer) (void)hipFree(p->d_tile_layer);
         free(p->h_offsets);
         delete p;
         return device_status(e, "plan device table");
@@ -170,6 +195,7 @@ void ga_plan_destroy(ga_plan* plan) {
     if (!plan) return;
     ga::Plan* p = reinterpret_cast<ga::Plan*>(plan);
     if (p->d_offsets) (void)hipFree(p->d_offsets);
+    if (p->d_tile_layer) (void)hipFree(p->d_tile_layer);
     free(p->h_offsets);
     delete p;
 }
@@ -201,6 +227,35 @@ ga_status ga_tree_reduce(const ga_plan* plan, const void* d_bucket, float* d_gra
     ga_status st = check_device(p);
     if (st != GA_OK) return st;
     return device_status(ga::launch_tree(*p, d_bucket, d_grad, sgd, d_w, d_v, stream), "tree_reduce launch");
+}
+
+ga_status ga_tree_reduce_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_grad, const ga_sgd* sgd,
+                                float* d_w, float* d_v, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs) return fail(GA_ERR_INVALID, "NULL argument");
+    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
+    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
+    if (((uintptr_t)d_layer_ptrs & 7u) || (d_grad && !aligned16(d_grad)) ||
+        (sgd && (!aligned16(d_w) || !aligned16(d_v))))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    const ga::Plan* p = as_plan(plan);
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_tree_layers(*p, d_layer_ptrs, d_grad, sgd, d_w, d_v, stream),
+                         "tree_reduce_layers launch");
+}
+
+ga_status ga_chunk_norm_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
+                               const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_residual || !d_keys) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (((uintptr_t)d_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_keys & 7u) ||
+        (d_prev_mask && ((uintptr_t)d_prev_mask & 3u)))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_chunk_norm_layers(*p, d_layer_ptrs, d_residual, d_prev_mask, d_keys, stream),
+                         "chunk_norm_layers launch");
 }
 
 ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_residual, const uint32_t* d_prev_mask,

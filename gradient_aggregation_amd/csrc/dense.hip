@@ -31,6 +31,11 @@ __device__ __forceinline__ uint4 load_leaf(const char* p) {
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 
+__device__ __forceinline__ uint4 load_leaf_at(uint64_t addr) {
+    const v4u x = __builtin_nontemporal_load(as_global<v4u>(addr));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 template <bool FP16>
 struct LeafVec;
 
@@ -129,6 +134,165 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
     epilogue<E>(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
 }
 
+// Zero-copy lazy-allreduce fusion for the dense path: the leaves are read
+// straight from every worker's per-layer tensors through the layer table.
+// A wavefront whose 64*E elements lie in one layer (the common case) resolves
+// the layer once and reads each worker's tensor with 128-bit loads (element
+// loads when a tensor is not 16-byte aligned); a wavefront that straddles a
+// layer boundary resolves the layer of every element.
+template <int LEV, bool FP16>
+__global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __restrict__ layer_ptrs,
+                                                          const int64_t* __restrict__ offsets,
+                                                          const uint32_t* __restrict__ tile_layer, int32_t L,
+                                                          int32_t W, int64_t P, float invW,
+                                                          float* __restrict__ grad, int32_t do_sgd, float lr,
+                                                          float mu, float* __restrict__ w,
+                                                          float* __restrict__ v) {
+    using LV = LeafVec<FP16>;
+    constexpr int E = LV::E;
+    constexpr int kEsz = FP16 ? 2 : 4;
+    using raw = typename LV::raw;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base =
+        ((int64_t)blockIdx.x * kThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
+    if (wave_base >= P) return;
+    const int64_t i0 = wave_base + (int64_t)lane * E;
+    const bool valid = i0 < P;
+
+    auto layer_of = [&](int64_t i) {
+        int32_t lo = 0, hi = L;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) >> 1;
+            if (offsets[mid + 1] <= i) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    };
+    // The plan's tile table gives the wavefront's layer in one scalar load.
+    const uint32_t tinfo = tile_layer[wave_base / (64 * E)];
+    const int32_t l0 = (int32_t)(tinfo & 0x7fffffffu);
+    const int64_t off0 = offsets[l0];
+    // Fast path: the wavefront's 64*E elements all exist, lie in layer l0 at an
+    // E-aligned offset, and every worker's tensor of that layer is 16-byte
+    // aligned (checked with one ballot per 64 workers).
+    bool fast = (tinfo >> 31) != 0u;
+    // For W < 256 the (at most four) 64-worker groups of addresses stay in
+    // registers from the alignment check to the loads.
+    constexpr int kGroups = LEV <= 8 ? 4 : 1;
+    uint64_t gaddr[kGroups];
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) gaddr[gi] = 0ull;
+    if (fast) {
+        for (int32_t g0 = 0; g0 < W; g0 += 64) {
+            const uint64_t a = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
+            fast = fast && __ballot((a & 15ull) != 0ull) == 0ull;
+            if (LEV <= 8) {
+#pragma unroll
+                for (int gi = 0; gi < kGroups; ++gi)
+                    if (gi == (g0 >> 6)) gaddr[gi] = a;
+            }
+        }
+    }
+
+    TreeAcc<LEV, E> tree;
+    uint32_t cnt = 0;
+    if (fast) {
+        for (int32_t g0 = 0; g0 < W; g0 += 64) {
+            // lane l holds worker (g0 + l)'s tensor address; each worker's
+            // address is then taken from its lane without a memory access
+            uint64_t mine = 0ull;
+            if (LEV <= 8) {
+#pragma unroll
+                for (int gi = 0; gi < kGroups; ++gi)
+                    if (gi == (g0 >> 6)) mine = gaddr[gi];
+            } else {
+                mine = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
+            }
+            const uint32_t mine_lo = (uint32_t)mine, mine_hi = (uint32_t)(mine >> 32);
+            const int32_t gn = W - g0 < 64 ? W - g0 : 64;
+            const int64_t byte_off = (i0 - off0) * kEsz;
+            for (int32_t u0 = 0; u0 < gn; u0 += kUnrollW) {
+                // All addresses first, then all loads with no branch between
+                // them, so the 16 loads are in flight together (past the group
+                // end the last worker is re-read and not pushed).
+                uint64_t addr[kUnrollW];
+#pragma unroll
+                for (int u = 0; u < kUnrollW; ++u) {
+                    const int ui = u0 + u < gn ? u0 + u : gn - 1;
+                    addr[u] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine_hi, ui) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)mine_lo, ui);
+                }
+                raw x[kUnrollW];
+#pragma unroll
+                for (int u = 0; u < kUnrollW; ++u) x[u] = load_leaf_at(addr[u] + (uint64_t)byte_off);
+#pragma unroll
+                for (int u = 0; u < kUnrollW; ++u) {
+                    if (u0 + u < gn) {
+                        float f[E];
+                        LV::widen(x[u], f);
+                        tree.push(f, cnt);
+                        ++cnt;
+                    }
+                }
+            }
+        }
+    } else {
+        // General path (the wavefront straddles a layer boundary, holds the
+        // tail, or meets an unaligned tensor): each lane resolves the layer of
+        // its own first element and, when its E elements lie in that layer at
+        // an E-aligned offset and the tensor is aligned, reads each worker
+        // with one 128-bit load, otherwise element by element; 8 workers in
+        // flight.
+        constexpr int kU = 8;
+        const int32_t la = valid ? layer_of(i0) : 0;
+        const int64_t oa = offsets[la], ea = offsets[la + 1];
+        const bool lane_vec = valid && i0 + E <= ea && (oa % E) == 0;
+        for (int32_t w0 = 0; w0 < W; w0 += kU) {
+            uint64_t ad[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                ad[u] = (w0 + u < W && valid) ? layer_ptrs[(int64_t)(w0 + u) * L + la] : 0ull;
+            raw x[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                x[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (w0 + u < W && valid) {
+                    if (lane_vec && (ad[u] & 15) == 0) {
+                        x[u] = load_leaf_at(ad[u] + (uint64_t)((i0 - oa) * kEsz));
+                    } else {
+                        uint32_t q[4] = {0u, 0u, 0u, 0u};
+                        for (int e = 0; e < E; ++e) {
+                            const int64_t i = i0 + e;
+                            if (i < P) {
+                                const int32_t l = i < ea ? la : layer_of(i);
+                                const uint64_t a = l == la ? ad[u] : layer_ptrs[(int64_t)(w0 + u) * L + l];
+                                const int64_t j = i - offsets[l];
+                                const uint32_t bits = FP16 ? (uint32_t)as_global<uint16_t>(a)[j]
+                                                           : as_global<uint32_t>(a)[j];
+                                if (FP16) q[e >> 1] |= bits << (16 * (e & 1));
+                                else q[e] = bits;
+                            }
+                        }
+                        x[u] = make_uint4(q[0], q[1], q[2], q[3]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (w0 + u < W) {
+                    float f[E];
+                    LV::widen(x[u], f);
+                    tree.push(f, cnt);
+                    ++cnt;
+                }
+            }
+        }
+    }
+    float s[E];
+    tree.result((uint32_t)W, s);
+    if (valid) epilogue<E>(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
+}
+
 __global__ __launch_bounds__(kThreads) void k_sgd(int64_t P, const float* __restrict__ g,
                                                   float* __restrict__ w, float* __restrict__ v,
                                                   float lr, float mu) {
@@ -171,6 +335,23 @@ hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const g
     return hipGetLastError();
 }
 
+template <int LEV>
+hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
+                                float* w, float* v, hipStream_t s) {
+    const int E = p.dtype == GA_FP16 ? 8 : 4;
+    const int64_t threads = (p.P + E - 1) / E;
+    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const float invW = (float)(1.0 / (double)p.W);
+    const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
+    if (p.dtype == GA_FP16)
+        hipLaunchKernelGGL((k_tree_layers<LEV, true>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets,
+                           p.d_tile_layer, p.L, p.W, p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    else
+        hipLaunchKernelGGL((k_tree_layers<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets,
+                           p.d_tile_layer, p.L, p.W, p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
@@ -180,6 +361,13 @@ hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_
     // tree for small W (fewer resident waves, same bytes in flight).
     if (p.W < (1 << 8)) return tree_dispatch<8>(p, bucket, grad, sgd, w, v, s);
     return tree_dispatch<11>(p, bucket, grad, sgd, w, v, s);
+}
+
+hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
+                              float* w, float* v, hipStream_t s) {
+    if (p.P == 0) return hipSuccess;
+    if (p.W < (1 << 8)) return tree_layers_dispatch<8>(p, layer_ptrs, grad, sgd, w, v, s);
+    return tree_layers_dispatch<11>(p, layer_ptrs, grad, sgd, w, v, s);
 }
 
 hipError_t launch_sgd(int64_t P, const float* g, float* w, float* v, const ga_sgd* sgd,

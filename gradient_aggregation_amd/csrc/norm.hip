@@ -1,7 +1,9 @@
 // Coarse-grained sparse communication, part 1 (GradientFlow, arXiv abstract:
 // only the important gradient chunks are transmitted): chunk norms.
 //
-// k_chunk_norm: one workgroup (256 threads) per (worker, chunk).  Each thread
+// k_chunk_norm: one workgroup (256 threads) per (worker, chunk).  The
+// gradient comes from the flat bucket, or (zero-copy lazy-allreduce fusion)
+// straight from the workers' per-layer tensors through the layer table.  Each thread
 // takes 8-element vectors (one 128-bit binary16 load of the gradient, two of
 // the binary32 residual), 4 vectors in flight; a = leaf + residual is written
 // back over the residual, and the chunk's key, the sum of a^2 in binary64
@@ -27,39 +29,30 @@ __device__ __forceinline__ double wave_sum(double x) {
 // ---------------------------------------------------------------------------
 // k_chunk_norm
 // ---------------------------------------------------------------------------
-template <bool FP16, bool LAZY>
-__global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
-    const void* __restrict__ bucket, float* __restrict__ resid, int64_t ld, int64_t P, int64_t C,
-    int32_t n_c, const uint32_t* __restrict__ prev_mask, int32_t mw, double* __restrict__ keys) {
-    const int64_t b = blockIdx.x;
-    const int32_t w = (int32_t)(b / n_c);
-    const int32_t c = (int32_t)(b - (int64_t)w * n_c);
-    const int64_t s = (int64_t)c * C;
-    const int64_t e = s + C < P ? s + C : P;
-    bool rzero = false;
-    if (LAZY) rzero = (prev_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
 
-    float* __restrict__ r = resid + (int64_t)w * ld;
-    double acc0 = 0.0, acc1 = 0.0;
-
-    // Body: 8-element vectors (chunk starts are multiples of 8).
-    const int64_t nvec = (e - s) >> 3;
+// Flat elements [ss, se) of one worker: gradient element i is src[i - soff]
+// (src typed by FP16), residual element i is r[i].  With vec_ok, ss is a
+// multiple of 8 and src + (ss - soff) is 16-byte aligned, so the body runs on
+// 8-element vectors; the rest goes element by element.
+template <bool FP16>
+__device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_t soff, bool vec_ok,
+                                             float* __restrict__ r, int64_t ss, int64_t se, bool rzero,
+                                             double& acc0, double& acc1) {
     constexpr int UN = 4;
+    const int64_t nvec = vec_ok ? (se - ss) >> 3 : 0;
     int64_t j = threadIdx.x;
     for (; j + (UN - 1) * kNormThreads < nvec; j += UN * kNormThreads) {
         float lf[UN][8];
         float4 r0[UN], r1[UN];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
-            const int64_t i = s + ((j + u * kNormThreads) << 3);
+            const int64_t i = ss + ((j + u * kNormThreads) << 3);
             if (FP16) {
-                const uint4 gv = *reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(bucket) + (int64_t)w * ld + i);
-                widen8(gv, lf[u]);
+                widen8(load_u4(static_cast<gptr<uint16_t>>(src) + (i - soff)), lf[u]);
             } else {
-                const float* gp = static_cast<const float*>(bucket) + (int64_t)w * ld + i;
-                const float4 g0 = *reinterpret_cast<const float4*>(gp);
-                const float4 g1 = *reinterpret_cast<const float4*>(gp + 4);
+                gptr<float> gp = static_cast<gptr<float>>(src) + (i - soff);
+                const float4 g0 = load_f4(gp);
+                const float4 g1 = load_f4(gp + 4);
                 lf[u][0] = g0.x; lf[u][1] = g0.y; lf[u][2] = g0.z; lf[u][3] = g0.w;
                 lf[u][4] = g1.x; lf[u][5] = g1.y; lf[u][6] = g1.z; lf[u][7] = g1.w;
             }
@@ -73,7 +66,7 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
-            const int64_t i = s + ((j + u * kNormThreads) << 3);
+            const int64_t i = ss + ((j + u * kNormThreads) << 3);
             float4 a0, a1;
             a0.x = lf[u][0] + r0[u].x; a0.y = lf[u][1] + r0[u].y;
             a0.z = lf[u][2] + r0[u].z; a0.w = lf[u][3] + r0[u].w;
@@ -92,12 +85,12 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
         }
     }
     for (; j < nvec; j += kNormThreads) {
-        const int64_t i = s + (j << 3);
+        const int64_t i = ss + (j << 3);
         float lf[8];
         if (FP16) {
-            widen8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(bucket) + (int64_t)w * ld + i), lf);
+            widen8(load_u4(static_cast<gptr<uint16_t>>(src) + (i - soff)), lf);
         } else {
-            const float* gp = static_cast<const float*>(bucket) + (int64_t)w * ld + i;
+            gptr<float> gp = static_cast<gptr<float>>(src) + (i - soff);
 #pragma unroll
             for (int q = 0; q < 8; ++q) lf[q] = gp[q];
         }
@@ -108,14 +101,52 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
             acc0 = fma((double)a, (double)a, acc0);
         }
     }
-    // Tail: fewer than 8 elements at the end of the last chunk.
-    for (int64_t i = s + (nvec << 3) + threadIdx.x; i < e; i += kNormThreads) {
-        float lf;
-        if (FP16) lf = widen1(static_cast<const uint16_t*>(bucket)[(int64_t)w * ld + i]);
-        else lf = static_cast<const float*>(bucket)[(int64_t)w * ld + i];
+    for (int64_t i = ss + (nvec << 3) + threadIdx.x; i < se; i += kNormThreads) {
+        const float lf = FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i - soff])
+                              : static_cast<gptr<float>>(src)[i - soff];
         const float a = lf + (rzero ? 0.f : r[i]);
         r[i] = a;
         acc0 = fma((double)a, (double)a, acc0);
+    }
+}
+
+// One workgroup per (worker w, chunk c).  LAYERS: the gradient is read from
+// the W*L per-layer tensors of the layer table (zero-copy fusion: the chunk's
+// elements are gathered from the layers it overlaps); otherwise from the
+// flat [W][ld] bucket.
+template <bool FP16, bool LAZY, bool LAYERS>
+__global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
+    const void* __restrict__ bucket, const uint64_t* __restrict__ layer_ptrs,
+    const int64_t* __restrict__ offsets, int32_t L, float* __restrict__ resid, int64_t ld, int64_t P,
+    int64_t C, int32_t n_c, const uint32_t* __restrict__ prev_mask, int32_t mw, double* __restrict__ keys) {
+    const int64_t b = blockIdx.x;
+    const int32_t w = (int32_t)(b / n_c);
+    const int32_t c = (int32_t)(b - (int64_t)w * n_c);
+    const int64_t s = (int64_t)c * C;
+    const int64_t e = s + C < P ? s + C : P;
+    bool rzero = false;
+    if (LAZY) rzero = (prev_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
+
+    float* __restrict__ r = resid + (int64_t)w * ld;
+    double acc0 = 0.0, acc1 = 0.0;
+    if (LAYERS) {
+        // first layer ending after s (uniform binary search)
+        int32_t lo = 0, hi = L;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) >> 1;
+            if (offsets[mid + 1] <= s) lo = mid + 1;
+            else hi = mid;
+        }
+        for (int32_t l = lo; l < L && offsets[l] < e; ++l) {
+            const int64_t off = offsets[l], end = offsets[l + 1];
+            const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
+            const bool vec_ok = (off & 7) == 0 && (addr & 15) == 0;
+            norm_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e,
+                               rzero, acc0, acc1);
+        }
+    } else {
+        const uint64_t row = reinterpret_cast<uint64_t>(bucket) + (uint64_t)(w * ld * (FP16 ? 2 : 4));
+        norm_segment<FP16>(as_global<void>(row), 0, true, r, s, e, rzero, acc0, acc1);
     }
 
     double t = wave_sum(acc0 + acc1);
@@ -131,27 +162,34 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     }
 }
 
-}  // namespace
-
-hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid, const uint32_t* prev_mask,
-                             double* keys, hipStream_t s) {
+template <bool LAYERS>
+hipError_t norm_dispatch(const Plan& p, const void* bucket, const uint64_t* layer_ptrs, float* resid,
+                         const uint32_t* prev_mask, double* keys, hipStream_t s) {
     const int64_t blocks = (int64_t)p.W * p.n_c;
     if (blocks == 0) return hipSuccess;
     const bool f16 = p.dtype == GA_FP16;
     const int32_t n_c = (int32_t)p.n_c;
-    if (f16 && prev_mask)
-        hipLaunchKernelGGL((k_chunk_norm<true, true>), dim3((unsigned)blocks), dim3(kNormThreads), 0, s,
-                           bucket, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys);
-    else if (f16)
-        hipLaunchKernelGGL((k_chunk_norm<true, false>), dim3((unsigned)blocks), dim3(kNormThreads), 0, s,
-                           bucket, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys);
-    else if (prev_mask)
-        hipLaunchKernelGGL((k_chunk_norm<false, true>), dim3((unsigned)blocks), dim3(kNormThreads), 0, s,
-                           bucket, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys);
-    else
-        hipLaunchKernelGGL((k_chunk_norm<false, false>), dim3((unsigned)blocks), dim3(kNormThreads), 0, s,
-                           bucket, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys);
+#define GA_NORM_LAUNCH(F, Z)                                                                                 \
+    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS>), dim3((unsigned)blocks), dim3(kNormThreads), 0, s, bucket, \
+                       layer_ptrs, p.d_offsets, p.L, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys)
+    if (f16 && prev_mask) GA_NORM_LAUNCH(true, true);
+    else if (f16) GA_NORM_LAUNCH(true, false);
+    else if (prev_mask) GA_NORM_LAUNCH(false, true);
+    else GA_NORM_LAUNCH(false, false);
+#undef GA_NORM_LAUNCH
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid, const uint32_t* prev_mask,
+                             double* keys, hipStream_t s) {
+    return norm_dispatch<false>(p, bucket, nullptr, resid, prev_mask, keys, s);
+}
+
+hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, float* resid,
+                                    const uint32_t* prev_mask, double* keys, hipStream_t s) {
+    return norm_dispatch<true>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s);
 }
 
 }  // namespace ga

@@ -41,14 +41,14 @@ __global__ __launch_bounds__(kThreads) void k_pack(const uint64_t* __restrict__ 
         const int64_t s = off > e0 ? off : e0;
         const int64_t t = offsets[l + 1] < e1 ? offsets[l + 1] : e1;
         const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
-        const T* __restrict__ src = reinterpret_cast<const T*>(addr);  // element i of the row is src[i - off]
+        gptr<T> __restrict__ src = as_global<T>(addr);  // element i of the row is src[i - off]
         const bool vec = (off % V) == 0 && (addr % kVecBytes) == 0;
         if (vec) {
             // s is a multiple of V here (e0 and off both are).
             const int64_t nv = (t - s) / V;
             for (int64_t j = threadIdx.x; j < nv; j += kThreads) {
                 const int64_t i = s + j * V;
-                *reinterpret_cast<uint4*>(row + i) = *reinterpret_cast<const uint4*>(src + (i - off));
+                *reinterpret_cast<uint4*>(row + i) = load_u4(src + (i - off));
             }
             for (int64_t i = s + nv * V + threadIdx.x; i < t; i += kThreads) row[i] = src[i - off];
         } else {

@@ -157,6 +157,17 @@ ga_status ga_tree_reduce(const ga_plan* plan, const void* d_bucket, float* d_gra
                          const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream);
 
 /*
+ * ga_tree_reduce with zero-copy fusion: the same result, with the leaves read
+ * straight from every worker's per-layer tensors instead of a packed bucket
+ * (lazy allreduce [GF] as one launch over all W*L tensors, no copy).
+ *   d_layer_ptrs: as in ga_bucket_pack (W*n_layers device addresses,
+ *                 worker-major).  16-byte aligned tensors are read with
+ *                 128-bit loads, others element by element.
+ */
+ga_status ga_tree_reduce_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_grad,
+                                const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream);
+
+/*
  * Coarse-grained sparse communication [GF], part 1 (sparse plan required):
  * for every worker w and chunk c,
  *   a[w][i] = fl32(leaf(bucket[w][i]) + r[w][i])  for i in chunk c
@@ -171,6 +182,15 @@ ga_status ga_tree_reduce(const ga_plan* plan, const void* d_bucket, float* d_gra
  */
 ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_residual,
                         const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream);
+
+/*
+ * ga_chunk_norm with zero-copy fusion: the gradient is read straight from the
+ * workers' per-layer tensors (d_layer_ptrs as in ga_bucket_pack); a chunk that
+ * spans several layers is assembled from each of them.  d_residual, the keys
+ * and the lazy-zero mode are as in ga_chunk_norm.
+ */
+ga_status ga_chunk_norm_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
+                               const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream);
 
 /*
  * Part 2: per worker, select the k most important chunks by key (the squared

@@ -51,3 +51,29 @@ def assert_same_bits(got, ref, name=""):
         i = int(np.flatnonzero(~same.ravel())[0])
         raise AssertionError("%s: %d mismatches, first at %d: %r vs %r" % (
             name, int((~same).sum()), i, got.ravel()[i], ref.ravel()[i]))
+
+
+def device_layers(rows: np.ndarray, numels, misalign=lambda w, l: 0):
+    """Copy each worker's gradient row, split into layers of `numels` elements,
+    into separate places of one device buffer, layer (w, l) starting
+    misalign(w, l) elements past a 16-byte boundary with gaps between layers.
+    Returns (buffer, int64 tensor of the W*L layer addresses, worker-major)."""
+    import torch
+    W = rows.shape[0]
+    isz = rows.dtype.itemsize
+    ti = {2: torch.int16, 4: torch.int32}[isz]
+    ni = {2: np.int16, 4: np.int32}[isz]
+    pad = 16 // isz
+    total = sum(n + 3 * pad for n in numels) * W
+    buf = torch.zeros(total, dtype=ti, device="cuda")
+    offs = np.cumsum([0] + list(numels))
+    ptrs, off = [], 0
+    for w in range(W):
+        for l, n in enumerate(numels):
+            s = off + misalign(w, l) % pad
+            src = np.ascontiguousarray(rows[w, offs[l]:offs[l + 1]]).view(ni)
+            buf[s:s + n].copy_(torch.from_numpy(src))
+            ptrs.append(buf.data_ptr() + s * isz)
+            off += n + 2 * pad
+            off += (-off) % pad
+    return buf, torch.tensor(ptrs, dtype=torch.int64, device="cuda")
