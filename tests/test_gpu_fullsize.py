@@ -2,10 +2,12 @@
 benchmark times, against the oracle run on the host cores.
 
 NiN-, GoogLeNet- and AlexNet-shaped dense aggregation are compared on every
-element.  The AlexNet-shaped W=128 sparse workload (3 consecutive steps,
-lazy-zero residual mode as benchmarked) is compared on every selected index,
-every key, every mean-gradient/weight/velocity element and the residual of a
-sample of workers."""
+element, from a packed bucket and from the per-layer tensors.  The
+AlexNet-shaped W=128 sparse workload is run as benchmarked (2048 per-layer
+tensors read with zero copy, 3 consecutive steps, lazy-zero residual with one
+reused mask buffer) and compared on every selected index, every key, every
+mean-gradient/weight/velocity element and the residual of a sample of
+workers."""
 import os
 import time
 
@@ -14,7 +16,8 @@ import pytest
 
 import oracle
 import workloads
-from helpers import KEY_RTOL, TOL_FP16_PATH, TOL_FP32, assert_close, assert_same_bits, host, to_dev
+from helpers import (KEY_RTOL, TOL_FP16_PATH, TOL_FP32, assert_close, assert_same_bits, device_layers, host,
+                     to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -33,8 +36,9 @@ def log(msg):
     print("[fullsize] %s" % msg, flush=True)
 
 
+@pytest.mark.parametrize("source", ["bucket", "layers"])
 @pytest.mark.parametrize("name", ["nin", "googlenet", "alexnet16"])
-def test_dense_full_size(ga, name):
+def test_dense_full_size(ga, name, source):
     wl = workloads.WORKLOADS[name]
     plan = ga.Plan(wl.W, wl.numels, wl.fp16)
     w_ref = workloads.weights(wl)
@@ -44,17 +48,23 @@ def test_dense_full_size(ga, name):
     for step in (1, 2):
         t0 = time.time()
         b = workloads.grad_bucket(wl, step, plan.ld)
-        bd = to_dev(b, wl.fp16)
+        if source == "layers":
+            src, ptrs = device_layers(b[:, :wl.P], wl.numels)
+        else:
+            src = to_dev(b, wl.fp16)
         g_ref = oracle.dense_step(b, wl.P, wl.fp16, wl.lr, wl.mu, w_ref, v_ref)
         del b
-        plan.tree_reduce(bd, gd, wd, vd, wl.lr, wl.mu)
+        if source == "layers":
+            plan.tree_reduce_layers(ptrs, gd, wd, vd, wl.lr, wl.mu)
+        else:
+            plan.tree_reduce(src, gd, wd, vd, wl.lr, wl.mu)
         torch.cuda.synchronize()
-        del bd
+        del src
         assert_close(host(gd), g_ref, TOL_FP16_PATH if wl.fp16 else TOL_FP32, "gbar")
         assert_same_bits(host(gd), g_ref, "gbar")
         assert_same_bits(host(wd), w_ref, "w")
         assert_same_bits(host(vd), v_ref, "v")
-        log("%s step %d ok in %.1fs" % (name, step, time.time() - t0))
+        log("%s (%s) step %d ok in %.1fs" % (name, source, step, time.time() - t0))
 
 
 def test_sparse_alexnet128_full_size(ga):
@@ -73,21 +83,23 @@ def test_sparse_alexnet128_full_size(ga):
     idx = torch.empty((wl.W, k), dtype=torch.int32, device="cuda")
     mask = torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda")
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
-    bd = torch.empty((wl.W, ld), dtype=torch.float16, device="cuda")
     sample = [0, 1, 63, 127]
     for step in (1, 2, 3):
         t0 = time.time()
         b = workloads.grad_bucket(wl, step, ld, seg=seg)
-        bd.copy_(torch.from_numpy(b.view(np.float16)))
-        log("step %d generated+uploaded in %.1fs" % (step, time.time() - t0))
+        buf, ptrs = device_layers(b[:, :P], wl.numels)
+        log("step %d generated+uploaded as %d layer tensors in %.1fs" % (step, wl.W * len(wl.numels),
+                                                                       time.time() - t0))
         t1 = time.time()
         res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         del b
         log("step %d oracle in %.1fs" % (step, time.time() - t1))
         # lazy-zero mode, one mask buffer reused across steps, as benchmarked
-        plan.chunk_norm_topk(bd, rd, keys, idx, mask, mask if step > 1 else None)
+        plan.chunk_norm_layers(ptrs, rd, keys, mask if step > 1 else None)
+        plan.chunk_topk(keys, idx, mask)
         plan.sparse_gather_reduce(rd, mask, False, gd, wd, vd, wl.lr, wl.mu)
         torch.cuda.synchronize()
+        del buf
         assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
         assert np.array_equal(host(idx), res.sel_idx), "selected chunk indices differ"
         assert np.array_equal(host(mask).view(np.uint32), res.sel_mask)
