@@ -60,6 +60,14 @@ def lib():
         L.ora_sparse_step.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _P,
                                       ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P,
                                       ctypes.c_float, ctypes.c_float, _P, _P, _P, ctypes.c_int32]
+        L.ora_round_f16.restype = ctypes.c_float
+        L.ora_round_f16.argtypes = [ctypes.c_float]
+        L.ora_ring_segment.restype = ctypes.c_int64
+        L.ora_ring_segment.argtypes = [ctypes.c_int32, ctypes.c_int64]
+        L.ora_reduce_variant.restype = ctypes.c_int
+        L.ora_reduce_variant.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _P,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, _P, _P,
+                                         ctypes.c_int32]
         L.ora_pack.restype = ctypes.c_int
         L.ora_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_int64, _P]
         _lib = L
@@ -168,6 +176,33 @@ def sparse_step(bucket: np.ndarray, P: int, fp16: bool, chunk: int, k: int, resi
     if rc != 0:
         raise RuntimeError("ora_sparse_step failed (%d)" % rc)
     return SparseResult(keys, sel_idx[:, :k], sel_mask, margin, gbar)
+
+
+ORDERS = {"tree": 0, "ps": 1, "ring": 2}
+
+
+def round_f16(x) -> np.ndarray:
+    """Nearest binary16 value of each binary32 value (ties to even), as binary32."""
+    L = lib()
+    flat = np.ascontiguousarray(x, np.float32).ravel()
+    return np.array([L.ora_round_f16(float(v)) for v in flat], np.float32).reshape(np.shape(x))
+
+
+def ring_segment(W: int, P: int) -> int:
+    return int(lib().ora_ring_segment(W, P))
+
+
+def reduce_variant(bucket: np.ndarray, P: int, fp16: bool, order: str, wire16: bool, lr: float = 0.0,
+                   mu: float = 0.0, w: Optional[np.ndarray] = None, v: Optional[np.ndarray] = None,
+                   threads: Optional[int] = None) -> np.ndarray:
+    """Mean gradient under another summation order and/or a binary16 wire."""
+    W, ld = bucket.shape
+    gbar = np.empty(P, np.float32)
+    rc = lib().ora_reduce_variant(W, P, ld, int(fp16), _ptr(bucket), ORDERS[order], int(wire16), lr, mu, _ptr(w),
+                                  _ptr(v), _ptr(gbar), _threads(threads))
+    if rc != 0:
+        raise RuntimeError("ora_reduce_variant failed (%d)" % rc)
+    return gbar
 
 
 def pack(layers, ld: int) -> np.ndarray:

@@ -355,6 +355,112 @@ int ora_sparse_step(int32_t W, int64_t P, int64_t ld, int32_t fp16, const void* 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Summation orders and wire precision of other aggregation schemes.        */
+/*                                                                          */
+/* Parameter server [FC sec. 6]: one server receives every worker's         */
+/* gradient and sums them; read here as adding them in worker order,        */
+/* ((x0 + x1) + x2) + ...                                                   */
+/* Ring allreduce [GF abstract]: the vector is cut into W segments; segment */
+/* s travels round the ring starting at worker s+1, each worker adding its  */
+/* own gradient to the partial sum it receives, and worker s completes it.  */
+/* Segment length Q = ceil(P/W) rounded up to 64 elements; segment s is     */
+/* [s*Q, min((s+1)*Q, P)).                                                  */
+/* Wire precision: with a binary16 wire (mixed-precision communication      */
+/* [GF abstract]) every value sent between workers is rounded to binary16   */
+/* and every add is binary32: in the tree the right operand of each add     */
+/* (the subtree sum that was sent) and the final broadcast; at the server   */
+/* the received gradients and the broadcast; on the ring each partial sum   */
+/* passed on and the broadcast.                                             */
+/* ------------------------------------------------------------------------ */
+
+/* binary32 -> nearest binary16 value (ties to even), as a binary32: the     */
+/* binary16 grid near |x| has spacing 2^(e-10) for 2^e <= |x| < 2^(e+1),    */
+/* e >= -14, and 2^-24 below 2^-14; x/q is rounded to an integer with rint  */
+/* (round-half-even) in binary64, where both the division by a power of two */
+/* and the product are exact.  Beyond the largest finite value the result   */
+/* is infinite (|x| >= 65520 rounds up).                                    */
+float ora_round_f16(float x) {
+    if (isnan(x) || isinf(x)) return x;
+    double a = fabs((double)x);
+    if (a >= 65520.0) return x > 0 ? INFINITY : -INFINITY;
+    if (a == 0.0) return x;
+    int e;
+    frexp(a, &e);          /* a = f * 2^e, 0.5 <= f < 1, so 2^(e-1) <= a < 2^e */
+    int ex = e - 1;
+    if (ex < -14) ex = -14;
+    double q = ldexp(1.0, ex - 10);
+    double m = rint((double)x / q);
+    return (float)(m * q);
+}
+
+static inline float wire(float x, int on) { return on ? ora_round_f16(x) : x; }
+
+/* Tree with a wire: T(lo,n) = T(lo,h) + R(T(lo+h,n-h)); the left subtree's */
+/* sum stays on the receiving worker, the right one was sent.               */
+static float tree_wire(const float* leaf, int lo, int n, int on) {
+    if (n == 1) return leaf[lo];
+    int h = 1;
+    while (2 * h < n) h *= 2;
+    float left = tree_wire(leaf, lo, h, on);
+    float right = tree_wire(leaf, lo + h, n - h, on);
+    return left + wire(right, on);
+}
+
+int64_t ora_ring_segment(int32_t W, int64_t P) {
+    int64_t q = (P + W - 1) / W;
+    return (q + 63) / 64 * 64;
+}
+
+struct var_ctx {
+    int W; int64_t P, ld; int fp16; const void* bucket; int order, wire; float lr, mu;
+    float* w; float* v; float* gbar; int threads; int failed;
+};
+
+static void variant_range(void* c, int64_t t0, int64_t t1) {
+    struct var_ctx* d = (struct var_ctx*)c;
+    float* leaf = (float*)malloc(sizeof(float) * (size_t)d->W);
+    if (!leaf) { d->failed = 1; return; }
+    int64_t Q = ora_ring_segment(d->W, d->P);
+    float invW = inv_workers(d->W);
+    for (int64_t t = t0; t < t1; ++t) {
+        int64_t i0 = d->P * t / d->threads, i1 = d->P * (t + 1) / d->threads;
+        for (int64_t i = i0; i < i1; ++i) {
+            for (int w = 0; w < d->W; ++w) leaf[w] = leaf_value(d->bucket, d->fp16, d->ld, w, i);
+            float S;
+            if (d->order == 0) {
+                S = tree_wire(leaf, 0, d->W, d->wire);
+            } else if (d->order == 1) {
+                S = wire(leaf[0], d->wire);
+                for (int w = 1; w < d->W; ++w) S = S + wire(leaf[w], d->wire);
+            } else {
+                int64_t seg = i / Q;
+                int first = (int)((seg + 1) % d->W);
+                S = leaf[first];
+                for (int j = 1; j < d->W; ++j) {
+                    int wk = (int)((seg + 1 + j) % d->W);
+                    S = wire(S, d->wire) + leaf[wk];
+                }
+            }
+            float g = wire(S, d->wire) * invW;
+            if (d->gbar) d->gbar[i] = g;
+            if (d->w) sgd_one(g, d->lr, d->mu, &d->w[i], &d->v[i]);
+        }
+    }
+    free(leaf);
+}
+
+/* order: 0 binary tree, 1 parameter server (worker order), 2 ring.
+ * wire16: nonzero for a binary16 wire.  Other arguments as ora_dense_step. */
+int ora_reduce_variant(int32_t W, int64_t P, int64_t ld, int32_t fp16, const void* bucket, int32_t order,
+                       int32_t wire16, float lr, float mu, float* w, float* v, float* gbar, int32_t threads) {
+    if (W < 1 || P < 0 || ld < P || !bucket || (!w) != (!v) || order < 0 || order > 2) return 1;
+    if (threads < 1) threads = 1;
+    struct var_ctx d = {W, P, ld, fp16, bucket, order, wire16 != 0, lr, mu, w, v, gbar, threads, 0};
+    parallel_for(threads, threads, variant_range, &d);
+    return d.failed ? 2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Lazy allreduce [GF abstract]: many per-layer gradient tensors are fused  */
 /* into one flat vector per worker so that one operation moves them all.    */
 /* Layer l of worker w lands at offset sum_{m<l} numel_m of row w.          */
