@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
     ap.add_argument("--source", choices=["layers", "bucket"], default="layers",
                     help="gradients as per-layer tensors fused with zero copy (default) or a packed bucket")
+    ap.add_argument("--order", choices=["tree", "server", "ring"], default="tree",
+                    help="dense workloads: summation order (parameter server, ring) for comparison")
+    ap.add_argument("--wire", choices=["f32", "f16"], default="f32",
+                    help="dense workloads: binary16 wire (every value sent between workers rounded)")
     ap.add_argument("--cpu-baseline", dest="cpu_baseline", action="store_true", default=True)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -112,6 +116,12 @@ def main():
 
     wl = workloads.WORKLOADS[args.workload]
     sparse = wl.mode == "sparse"
+    variant = args.order != "tree" or args.wire != "f32"
+    if variant:
+        if sparse:
+            print("--order/--wire apply to the dense workloads", file=sys.stderr)
+            sys.exit(2)
+        args.source = "bucket"      # the comparison schemes read a packed bucket
     plan = ga.Plan(wl.W, wl.numels, wl.fp16, chunk=wl.chunk, keep_ratio=wl.rho)
     P, ld, W = wl.P, plan.ld, wl.W
     thr = host_threads()
@@ -194,7 +204,9 @@ def main():
             if rec:
                 e[3].record(stream)
         else:
-            if layers_src:
+            if variant:
+                plan.reduce_variant(b, args.order, args.wire == "f16", None, wd, vd, wl.lr, wl.mu)
+            elif layers_src:
                 plan.tree_reduce_layers(b, None, wd, vd, wl.lr, wl.mu)
             else:
                 plan.tree_reduce(b, None, wd, vd, wl.lr, wl.mu)
@@ -236,8 +248,9 @@ def main():
     value = b_alg / (ms_step * 1e-3) / 1e9
     dom_ms = per_kernel[dom]["mean_ms"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
-                               {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom])
+    traffic = None if variant else measured_traffic(
+        args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
+        {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom])
 
     result = {
         "metric": METRIC,
@@ -260,6 +273,7 @@ def main():
             "residual_mode": "lazy-zero" if sparse else None, "gradient_batches": nb,
             "fusion": "zero-copy read of %d per-layer tensors" % (W * len(wl.numels)) if layers_src
                       else "pre-packed bucket",
+            "order": args.order, "wire": args.wire,
             "parallelism": "1 GPU, W workers as HBM buffers",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -268,7 +282,8 @@ def main():
         "grad_input_GBps": round(W * P * b_in / (ms_step * 1e-3) / 1e9, 2),
         "kernels": per_kernel,
         "roofline": {
-            "kernel": {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom],
+            "kernel": {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom] if not variant
+                      else "k_variant_" + ("tree" if args.order == "tree" else "seq"),
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],

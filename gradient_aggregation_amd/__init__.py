@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libgradagg.so")
 
 GA_OK, GA_ERR_INVALID, GA_ERR_ALIGN, GA_ERR_DEVICE, GA_ERR_UNSUPPORTED = range(5)
 GA_FP32, GA_FP16 = 0, 1
+ORDERS = {"tree": 0, "server": 1, "ring": 2}
 MAX_WORKERS = 1024
 MAX_CHUNKS = 65536
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.ga_tree_reduce_layers.argtypes = [_VP, _VP, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
         L.ga_chunk_norm_layers.restype = st
         L.ga_chunk_norm_layers.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_reduce_variant.restype = st
+        L.ga_reduce_variant.argtypes = [_VP, _VP, st, ctypes.c_int32, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
         L.ga_chunk_norm.restype = st
         L.ga_chunk_norm.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
         L.ga_chunk_topk.restype = st
@@ -227,6 +230,17 @@ class Plan:
                                            _dev(grad, torch.float32, self.P, "grad"), sgd,
                                            _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
                                            _stream_ptr()))
+
+    def reduce_variant(self, bucket, order: str = "tree", wire16: bool = False, grad=None, w=None, v=None,
+                       lr: Optional[float] = None, mu: Optional[float] = None) -> None:
+        """Dense aggregation in another summation order ("tree", "server" or
+        "ring"), optionally with a binary16 wire."""
+        torch = _torch()
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_reduce_variant(self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),
+                                       ORDERS[order], int(bool(wire16)), _dev(grad, torch.float32, self.P, "grad"),
+                                       sgd, _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
+                                       _stream_ptr()))
 
     def chunk_norm_layers(self, layer_ptrs, resid, keys, prev_mask=None) -> None:
         """chunk_norm reading the gradient straight from the per-layer tensors."""

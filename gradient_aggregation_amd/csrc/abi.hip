@@ -258,6 +258,21 @@ ga_status ga_chunk_norm_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs
                          "chunk_norm_layers launch");
 }
 
+ga_status ga_reduce_variant(const ga_plan* plan, const void* d_bucket, ga_order order, int32_t wire_fp16, float* d_grad,
+                            const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream) {
+    if (!plan || !d_bucket) return fail(GA_ERR_INVALID, "NULL argument");
+    if (order != GA_ORDER_TREE && order != GA_ORDER_SERVER && order != GA_ORDER_RING)
+        return fail(GA_ERR_INVALID, "unknown order %d", (int)order);
+    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
+    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
+    if (!aligned16(d_bucket)) return fail(GA_ERR_ALIGN, "bucket not 16-byte aligned");
+    const ga::Plan* p = as_plan(plan);
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_variant(*p, d_bucket, (int)order, wire_fp16 != 0, d_grad, sgd, d_w, d_v, stream),
+                         "reduce_variant launch");
+}
+
 ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_residual, const uint32_t* d_prev_mask,
                         double* d_keys, hipStream_t stream) {
     if (!plan || !d_bucket || !d_residual || !d_keys) return fail(GA_ERR_INVALID, "NULL argument");

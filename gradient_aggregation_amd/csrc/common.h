@@ -34,6 +34,8 @@ hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, f
                                     const uint32_t* prev_mask, double* keys, hipStream_t s);
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
+hipError_t launch_variant(const Plan& p, const void* bucket, int order, int wire16, float* grad, const ga_sgd* sgd,
+                          float* w, float* v, hipStream_t s);
 hipError_t launch_topk(const Plan& p, const double* keys, int32_t* sel_idx, uint32_t* sel_mask,
                        hipStream_t s);
 hipError_t launch_sparse_gather(const Plan& p, float* resid, const uint32_t* sel_mask,

@@ -23,7 +23,13 @@
 
 namespace ga {
 
-template <int LEV, int E>
+// Nearest binary16 value of a binary32 value (round to nearest even), as binary32.
+__device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
+
+// WIRE: every subtree sum that travels to another worker is binary16 - the
+// right operand of each add is rounded to binary16 first (the left operand is
+// the receiving worker's own partial sum and stays binary32).
+template <int LEV, int E, bool WIRE = false>
 struct TreeAcc {
     float acc[LEV][E];
 
@@ -43,7 +49,7 @@ struct TreeAcc {
         if constexpr (L < LEV) {
             if (cnt & (1u << L)) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) x[e] = acc[L][e] + x[e];
+                for (int e = 0; e < E; ++e) x[e] = acc[L][e] + (WIRE ? round_f16(x[e]) : x[e]);
                 push_from<L + 1>(x, cnt);
             } else {
 #pragma unroll
@@ -61,7 +67,7 @@ struct TreeAcc {
                     for (int e = 0; e < E; ++e) out[e] = acc[L][e];
                 } else {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) out[e] = acc[L][e] + out[e];
+                    for (int e = 0; e < E; ++e) out[e] = acc[L][e] + (WIRE ? round_f16(out[e]) : out[e]);
                 }
                 have = true;
             }

@@ -75,6 +75,9 @@ typedef enum {
 
 typedef enum { GA_FP32 = 0, GA_FP16 = 1 } ga_dtype;
 
+/* Summation orders of ga_reduce_variant. */
+typedef enum { GA_ORDER_TREE = 0, GA_ORDER_SERVER = 1, GA_ORDER_RING = 2 } ga_order;
+
 /* Momentum SGD hyper-parameters (Caffe form, see ga_sgd_momentum_apply). */
 typedef struct {
     float lr;
@@ -166,6 +169,26 @@ ga_status ga_tree_reduce(const ga_plan* plan, const void* d_bucket, float* d_gra
  */
 ga_status ga_tree_reduce_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_grad,
                                 const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream);
+
+/*
+ * Dense aggregation under the other schemes of the pages, for comparison with
+ * the tree (same bucket, mean and SGD as ga_tree_reduce):
+ *   GA_ORDER_TREE    the tree of ga_tree_reduce [FC sec. 6];
+ *   GA_ORDER_SERVER  a parameter server sums the gradients it receives, in
+ *                    worker order: ((x0 + x1) + x2) + ... [FC sec. 6];
+ *   GA_ORDER_RING    ring allreduce [GF]: the vector is cut into W segments of
+ *                    Q = ceil(P/W) rounded up to 64 elements; segment s is
+ *                    summed starting at worker s+1, each worker adding its
+ *                    value to the partial sum it receives, worker s last.
+ * wire_fp16 != 0: binary16 communication [GF] - every value sent between
+ * workers is rounded to binary16 (nearest, ties to even), every add is
+ * binary32: the right operand of each tree add, each ring partial sum passed
+ * on, the gradients the server receives, and the broadcast sum, which is
+ * rounded before the mean.  With GA_ORDER_TREE and wire_fp16 == 0 the result
+ * equals ga_tree_reduce bit for bit.
+ */
+ga_status ga_reduce_variant(const ga_plan* plan, const void* d_bucket, ga_order order, int32_t wire_fp16,
+                            float* d_grad, const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream);
 
 /*
  * Coarse-grained sparse communication [GF], part 1 (sparse plan required):

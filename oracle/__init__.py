@@ -178,7 +178,7 @@ def sparse_step(bucket: np.ndarray, P: int, fp16: bool, chunk: int, k: int, resi
     return SparseResult(keys, sel_idx[:, :k], sel_mask, margin, gbar)
 
 
-ORDERS = {"tree": 0, "ps": 1, "ring": 2}
+ORDERS = {"tree": 0, "ps": 1, "server": 1, "ring": 2}
 
 
 def round_f16(x) -> np.ndarray:
