@@ -61,6 +61,20 @@ def parse():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy (one-layer pack) of known size, for counter calibration")
+    ap.add_argument("--overlap", action="store_true",
+                    help="dense workloads: time a stand-in backward pass (one weight-gradient GEMM per layer, "
+                         "last layer first) with the multi-bucket reduction overlapped on a second stream")
+    ap.add_argument("--bucket-mb", default="1,4,16,100000",
+                    help="--overlap: bucket thresholds to compare, MiB per worker")
+    ap.add_argument("--reduce-workgroups", default="0,512",
+                    help="--overlap: grid caps of the bucket reductions to compare (0: full grid)")
+    ap.add_argument("--producer", choices=["gemm", "dense", "copy"], default="gemm",
+                    help="--overlap: each layer's gradients come from its weight-gradient GEMM (gemm), from "
+                         "the same flops as square 4096^3 GEMMs plus a copy of a staged gradient (dense), or "
+                         "from the copy alone (copy)")
+    ap.add_argument("--producer-batch", type=int, default=64,
+                    help="--overlap gemm: samples per worker; a layer's weight-gradient GEMM reduces over "
+                         "batch x output positions")
     ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the "
                                                     "dominant kernel (from rocprofv3 counters); default: "
                                                     "profiles/traffic_<workload>.json")
@@ -112,6 +126,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.overlap:
+        run_overlap(args)
         return
 
     wl = workloads.WORKLOADS[args.workload]
@@ -250,7 +267,7 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = None if variant else measured_traffic(
         args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
-        {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom])
+        "k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree")
 
     result = {
         "metric": METRIC,
@@ -282,7 +299,7 @@ def main():
         "grad_input_GBps": round(W * P * b_in / (ms_step * 1e-3) / 1e9, 2),
         "kernels": per_kernel,
         "roofline": {
-            "kernel": {"chunk_norm": "k_chunk_norm", "tree_sgd": "k_tree"}[dom] if not variant
+            "kernel": ("k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree") if not variant
                       else "k_variant_" + ("tree" if args.order == "tree" else "seq"),
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -297,6 +314,182 @@ def main():
 
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, plan, host_first, w_init, thr)
+    print(json.dumps(result), flush=True)
+
+
+def run_overlap(args):
+    """Multi-bucket lazy allreduce overlapped with a stand-in backward pass.
+
+    The producer writes every layer's gradients for all W workers, last layer
+    first, each layer as one batched GEMM dW[w] = dY[w] X[w] of the layer's
+    [out, in] weight shape (in = fan-in; 1 for a bias) whose reduction length
+    K is the per-worker batch times the layer's output positions (AlexNet:
+    55x55, 27x27 and 13x13 for conv1, conv2 and conv3-5, 1 for the fully
+    connected layers; other workloads: 1), the weight-gradient half of a
+    backward pass.  With --producer dense the same flops run as square
+    4096 x 4096 x 4096 GEMMs (compute-bound, little HBM traffic) followed by a
+    copy of a staged gradient into the layer; with --producer copy only the
+    copy runs.  The reduction runs per bucket on a second
+    stream, each bucket waiting on the event the producer records once the
+    bucket's layers are written.  Times (HIP events, mean over --steps):
+      T_prod     producer alone
+      T_red      the one-launch zero-copy reduction alone (+ SGD)
+      T_serial   producer, then the one-launch reduction, on one stream
+      T_overlap  producer and per-bucket reductions on two streams
+    (median over --steps rounds that run the five in turn).
+    overlap efficiency = (T_serial - T_overlap) / min(T_prod, T_red): 1 when
+    the shorter of the two is hidden entirely, 0 when nothing overlaps."""
+    import torch
+    import gradient_aggregation_amd as ga
+    import workloads
+    wl = workloads.WORKLOADS[args.workload if args.workload != "alexnet128_sparse" else "alexnet16"]
+    if wl.mode != "dense":
+        print("--overlap applies to the dense workloads", file=sys.stderr)
+        sys.exit(2)
+    W, P, L = wl.W, wl.P, len(wl.numels)
+    gdt = torch.float16 if wl.fp16 else torch.float32
+    esz = 2 if wl.fp16 else 4
+    plan = ga.Plan(W, wl.numels, wl.fp16)
+    torch.manual_seed(1)
+    shapes = []
+    for shp in wl.layers:
+        out = int(shp[0])
+        inn = int(np.prod(shp[1:])) if len(shp) > 1 else 1
+        shapes.append((out, inn))
+    positions = [1] * L
+    if list(wl.layers) == list(workloads.ALEXNET_LAYERS):
+        positions = [55 * 55] * 2 + [27 * 27] * 2 + [13 * 13] * 6 + [1] * 6
+    Ks = [args.producer_batch * p for p in positions]
+    # layer l of all workers: one [W, ldl] tensor, rows 16-byte aligned
+    lds = [(n + 7) // 8 * 8 for n in wl.numels]
+    layer_t = [torch.zeros((W, ld), dtype=gdt, device="cuda") for ld in lds]
+    ptrs = torch.tensor([layer_t[l].data_ptr() + w * lds[l] * esz for w in range(W) for l in range(L)],
+                        dtype=torch.int64, device="cuda")
+    if args.producer == "gemm":
+        A, B = [], []
+        for l, (o, i) in enumerate(shapes):
+            sc = 1.0 / np.sqrt(Ks[l])
+            A.append(torch.empty((W, o, Ks[l]), dtype=gdt, device="cuda").uniform_(-sc, sc))
+            B.append(torch.empty((W, Ks[l], i), dtype=gdt, device="cuda").uniform_(-1e-2, 1e-2))
+        tmp = [None if lds[l] == wl.numels[l] else torch.empty((W,) + shapes[l], dtype=gdt, device="cuda")
+               for l in range(L)]
+        flops = float(sum(2.0 * Ks[l] * W * wl.numels[l] for l in range(L)))
+    else:
+        stage = [torch.randn((W, ld), device="cuda").mul_(1e-3).to(gdt) for ld in lds]
+        flops = 0.0
+        reps_l = [0] * L
+        if args.producer == "dense":
+            n = 4096
+            X = torch.empty((n, n), dtype=gdt, device="cuda").uniform_(-0.02, 0.02)
+            Y = torch.empty((n, n), dtype=gdt, device="cuda").uniform_(-0.02, 0.02)
+            Z = torch.empty((n, n), dtype=gdt, device="cuda")
+            reps_l = [int(round(2.0 * Ks[l] * W * wl.numels[l] / (2.0 * n ** 3))) for l in range(L)]
+            flops = float(sum(reps_l)) * 2.0 * n ** 3
+
+    def produce(l):
+        if args.producer == "gemm":
+            o, i = shapes[l]
+            if tmp[l] is None:
+                torch.bmm(A[l], B[l], out=layer_t[l].view(W, o, i))
+            else:
+                torch.bmm(A[l], B[l], out=tmp[l])
+                layer_t[l][:, :wl.numels[l]].copy_(tmp[l].view(W, -1))
+        else:
+            for _ in range(reps_l[l]):
+                torch.mm(X, Y, out=Z)
+            layer_t[l].copy_(stage[l])
+
+    wd = torch.from_numpy(workloads.weights(wl)).cuda()
+    vd = torch.zeros(P, dtype=torch.float32, device="cuda")
+    main = torch.cuda.current_stream()
+    s_prod, s_red = torch.cuda.Stream(), torch.cuda.Stream()
+    lr, mu = wl.lr, wl.mu
+
+    def timed_interleaved(fns, reps):
+        """Median time of each function, the functions run in turn so that
+        clock and power drift affect them alike."""
+        for _ in range(args.warmup):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+              for _ in range(reps)]
+        for r in range(reps):
+            for j, fn in enumerate(fns):
+                ev[r][j][0].record(main)
+                fn()
+                ev[r][j][1].record(main)
+        torch.cuda.synchronize()
+        return [float(np.median([ev[r][j][0].elapsed_time(ev[r][j][1]) for r in range(reps)]))
+                for j in range(len(fns))]
+
+    def prod_all():
+        for l in range(L - 1, -1, -1):
+            produce(l)
+
+    def red_all():
+        plan.tree_reduce_layers(ptrs, None, wd, vd, lr, mu)
+
+    def serial():
+        prod_all()
+        red_all()
+
+    reps = args.steps
+    rows = []
+    caps = [int(x) for x in args.reduce_workgroups.split(",") if x]
+    for mb in [float(x) for x in args.bucket_mb.split(",") if x]:
+        bk = ga.Buckets(plan, int(mb * (1 << 20)))
+        first_to_bucket = {r[0]: i for i, r in enumerate(bk.ranges)}
+        ready = [torch.cuda.Event() for _ in range(bk.count)]
+        start_ev, done_p, done_r = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
+        for cap in caps:
+            def overlapped():
+                start_ev.record(main)
+                s_prod.wait_event(start_ev)
+                s_red.wait_event(start_ev)
+                with torch.cuda.stream(s_prod):
+                    for l in range(L - 1, -1, -1):
+                        produce(l)
+                        if l in first_to_bucket:
+                            ready[first_to_bucket[l]].record(s_prod)
+                    done_p.record(s_prod)
+                with torch.cuda.stream(s_red):
+                    for b in range(bk.count):
+                        bk.reduce_layers(b, ptrs, ready[b], None, wd, vd, lr, mu, max_workgroups=cap)
+                    done_r.record(s_red)
+                main.wait_event(done_p)
+                main.wait_event(done_r)
+
+            def buckets_alone():
+                for b in range(bk.count):
+                    bk.reduce_layers(b, ptrs, None, None, wd, vd, lr, mu, max_workgroups=cap)
+
+            t_prod, t_red, t_bk, t_serial, t_ov = timed_interleaved(
+                [prod_all, red_all, buckets_alone, serial, overlapped], reps)
+            eff = (t_serial - t_ov) / min(t_prod, t_red)
+            rows.append({"bucket_mib": mb, "buckets": bk.count, "max_workgroups": cap,
+                         "T_prod_ms": round(t_prod, 4), "T_red_ms": round(t_red, 4),
+                         "T_red_buckets_ms": round(t_bk, 4), "T_serial_ms": round(t_serial, 4),
+                         "T_overlap_ms": round(t_ov, 4), "hidden_ms": round(t_prod + t_red - t_ov, 4),
+                         "efficiency": round(eff, 3)})
+            log("bucket %g MiB (%d buckets), grid cap %d: T_prod %.3f, T_red %.3f (buckets %.3f), T_serial %.3f, "
+                "T_overlap %.3f ms; hidden %.3f ms; efficiency %.2f" % (
+                    mb, bk.count, cap, t_prod, t_red, t_bk, t_serial, t_ov, t_prod + t_red - t_ov, eff))
+        bk.close()
+    best = max(rows, key=lambda r: r["efficiency"])
+    b_alg = W * P * esz + 16 * P
+    result = {
+        "metric": "computation/aggregation overlap efficiency (T_serial - T_overlap) / min(T_prod, T_red)",
+        "value": best["efficiency"], "unit": "fraction", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": best["T_overlap_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "W": W, "P": P, "grad_dtype": "f16" if wl.fp16 else "f32",
+                   "producer": args.producer,
+                   "producer_batch": args.producer_batch if args.producer != "copy" else None,
+                   "producer_tflop": round(flops / 1e12, 4), "parallelism": "1 GPU, W workers as HBM buffers"},
+        "T_red_GBps": round(b_alg / (best["T_red_ms"] * 1e-3) / 1e9, 1),
+        "buckets": rows,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -90,6 +90,19 @@ def lib() -> ctypes.CDLL:
                                               _VP]
         L.ga_sgd_momentum_apply.restype = st
         L.ga_sgd_momentum_apply.argtypes = [ctypes.c_int64, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP]
+        L.ga_bucket_boundaries.restype = st
+        L.ga_bucket_boundaries.argtypes = [ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP]
+        L.ga_buckets_create.restype = st
+        L.ga_buckets_create.argtypes = [_VP, ctypes.c_int64, _VP]
+        L.ga_buckets_destroy.restype = None
+        L.ga_buckets_destroy.argtypes = [_VP]
+        L.ga_buckets_count.restype = ctypes.c_int32
+        L.ga_buckets_count.argtypes = [_VP]
+        L.ga_bucket_range.restype = st
+        L.ga_bucket_range.argtypes = [_VP, ctypes.c_int32, _VP, _VP, _VP, _VP]
+        L.ga_bucket_reduce_layers.restype = st
+        L.ga_bucket_reduce_layers.argtypes = [_VP, ctypes.c_int32, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP, _VP,
+                                              ctypes.c_int32, _VP]
         _lib = L
     return _lib
 
@@ -111,6 +124,17 @@ def compute_info(W: int, layer_numels: Sequence[int], fp16: bool, chunk: int = 0
     _check(lib().ga_plan_compute_info(W, len(layer_numels), arr, GA_FP16 if fp16 else GA_FP32, chunk,
                                       keep_ratio, ctypes.byref(info)))
     return info
+
+
+def bucket_boundaries(layer_numels: Sequence[int], fp16: bool, bucket_bytes: int):
+    """First layer of every bucket, the bucket holding the last layer first
+    (host only; the rule is ga_bucket_boundaries')."""
+    n = len(layer_numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in layer_numels])
+    first = (ctypes.c_int32 * max(n, 1))()
+    nb = ctypes.c_int32(0)
+    _check(lib().ga_bucket_boundaries(n, arr, 2 if fp16 else 4, int(bucket_bytes), first, ctypes.byref(nb)))
+    return [int(first[b]) for b in range(nb.value)]
 
 
 # ----------------------------------------------------------------------------
@@ -284,6 +308,54 @@ class Plan:
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), int(bool(zero_selected)),
             _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
             _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
+
+
+class Buckets:
+    """Multi-bucket schedule of a plan: layers grouped from the last one down
+    into buckets of at least bucket_bytes per worker, each reduced on its own
+    once its layers are ready."""
+
+    def __init__(self, plan: Plan, bucket_bytes: int):
+        h = _VP()
+        _check(lib().ga_buckets_create(plan._h, int(bucket_bytes), ctypes.byref(h)))
+        self._h = h
+        self.plan = plan
+        self.count = int(lib().ga_buckets_count(h))
+        self.ranges = []
+        for b in range(self.count):
+            f, n, e0, e1 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+            _check(lib().ga_bucket_range(h, b, ctypes.byref(f), ctypes.byref(n), ctypes.byref(e0),
+                                         ctypes.byref(e1)))
+            self.ranges.append((f.value, n.value, e0.value, e1.value))
+
+    def __len__(self) -> int:
+        return self.count
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().ga_buckets_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reduce_layers(self, b: int, layer_ptrs, ready=None, grad=None, w=None, v=None,
+                      lr: Optional[float] = None, mu: Optional[float] = None, max_workgroups: int = 0) -> None:
+        """Reduce bucket b on the current stream, after `ready` (a
+        torch.cuda.Event, or None) has completed; max_workgroups > 0 caps the
+        grid."""
+        torch = _torch()
+        p = self.plan
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        ev = None if ready is None else ready.cuda_event
+        _check(lib().ga_bucket_reduce_layers(self._h, int(b),
+                                             _dev(layer_ptrs, torch.int64, p.W * len(p.layer_numels), "layer_ptrs"),
+                                             ev, _dev(grad, torch.float32, p.P, "grad"), sgd,
+                                             _dev(w, torch.float32, p.P, "w"), _dev(v, torch.float32, p.P, "v"),
+                                             int(max_workgroups), _stream_ptr()))
 
 
 def sgd_momentum_apply(grad, w, v, lr: float, mu: float) -> None:

@@ -104,6 +104,12 @@ ga_status check_device(const ga::Plan* p) {
 
 }  // namespace
 
+namespace ga {
+// Record a failure message for ga_last_error (used by the other ABI sources).
+ga_status api_fail(ga_status s, const char* msg) { return fail(s, "%s", msg); }
+ga_status api_ok() { return ok(); }
+}  // namespace ga
+
 extern "C" {
 
 int32_t ga_abi_version(void) { return GA_ABI_VERSION; }

@@ -25,6 +25,10 @@ struct Plan {
     int64_t tile_elems;
 };
 
+// ---- ABI error reporting (defined in abi.hip) ---------------------------
+ga_status api_fail(ga_status s, const char* msg);
+ga_status api_ok();
+
 // ---- launchers (each returns hipSuccess or the launch error) -------------
 hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd,
                        float* w, float* v, hipStream_t s);
@@ -34,6 +38,12 @@ hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, f
                                     const uint32_t* prev_mask, double* keys, hipStream_t s);
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
+// launch_tree_layers over a sub-list of layers: worker w's layer l is entry
+// w*tbl_stride + tbl_first + l of the layer table; max_blocks > 0 caps the
+// grid (the workgroups then stride over the blocks of elements).
+hipError_t launch_tree_layers_sub(const Plan& p, const uint64_t* layer_ptrs, int32_t tbl_stride, int32_t tbl_first,
+                                  float* grad, const ga_sgd* sgd, float* w, float* v, int32_t max_blocks,
+                                  hipStream_t s);
 hipError_t launch_variant(const Plan& p, const void* bucket, int order, int wire16, float* grad, const ga_sgd* sgd,
                           float* w, float* v, hipStream_t s);
 hipError_t launch_topk(const Plan& p, const double* keys, int32_t* sel_idx, uint32_t* sel_mask,

@@ -141,20 +141,19 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
 // loads when a tensor is not 16-byte aligned); a wavefront that straddles a
 // layer boundary resolves the layer of every element.
 template <int LEV, bool FP16>
-__global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __restrict__ layer_ptrs,
-                                                          const int64_t* __restrict__ offsets,
-                                                          const uint32_t* __restrict__ tile_layer, int32_t L,
-                                                          int32_t W, int64_t P, float invW,
-                                                          float* __restrict__ grad, int32_t do_sgd, float lr,
-                                                          float mu, float* __restrict__ w,
-                                                          float* __restrict__ v) {
+__device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* __restrict__ layer_ptrs,
+                                                  const int64_t* __restrict__ offsets,
+                                                  const uint32_t* __restrict__ tile_layer, int32_t L,
+                                                  int32_t tbl_stride, int32_t tbl_first, int32_t W, int64_t P,
+                                                  float invW, float* __restrict__ grad, int32_t do_sgd, float lr,
+                                                  float mu, float* __restrict__ w, float* __restrict__ v) {
     using LV = LeafVec<FP16>;
     constexpr int E = LV::E;
     constexpr int kEsz = FP16 ? 2 : 4;
     using raw = typename LV::raw;
     const int lane = threadIdx.x & 63;
     const int64_t wave_base =
-        ((int64_t)blockIdx.x * kThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
+        (blk * kThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
     if (wave_base >= P) return;
     const int64_t i0 = wave_base + (int64_t)lane * E;
     const bool valid = i0 < P;
@@ -184,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __rest
     for (int gi = 0; gi < kGroups; ++gi) gaddr[gi] = 0ull;
     if (fast) {
         for (int32_t g0 = 0; g0 < W; g0 += 64) {
-            const uint64_t a = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
+            const uint64_t a = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * tbl_stride + tbl_first + l0] : 0ull;
             fast = fast && __ballot((a & 15ull) != 0ull) == 0ull;
             if (LEV <= 8) {
 #pragma unroll
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __rest
                 for (int gi = 0; gi < kGroups; ++gi)
                     if (gi == (g0 >> 6)) mine = gaddr[gi];
             } else {
-                mine = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
+                mine = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * tbl_stride + tbl_first + l0] : 0ull;
             }
             const uint32_t mine_lo = (uint32_t)mine, mine_hi = (uint32_t)(mine >> 32);
             const int32_t gn = W - g0 < 64 ? W - g0 : 64;
@@ -251,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __rest
             uint64_t ad[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                ad[u] = (w0 + u < W && valid) ? layer_ptrs[(int64_t)(w0 + u) * L + la] : 0ull;
+                ad[u] = (w0 + u < W && valid) ? layer_ptrs[(int64_t)(w0 + u) * tbl_stride + tbl_first + la] : 0ull;
             raw x[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
@@ -265,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __rest
                             const int64_t i = i0 + e;
                             if (i < P) {
                                 const int32_t l = i < ea ? la : layer_of(i);
-                                const uint64_t a = l == la ? ad[u] : layer_ptrs[(int64_t)(w0 + u) * L + l];
+                                const uint64_t a = l == la ? ad[u] : layer_ptrs[(int64_t)(w0 + u) * tbl_stride + tbl_first + l];
                                 const int64_t j = i - offsets[l];
                                 const uint32_t bits = FP16 ? (uint32_t)as_global<uint16_t>(a)[j]
                                                            : as_global<uint32_t>(a)[j];
@@ -291,6 +290,35 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __rest
     float s[E];
     tree.result((uint32_t)W, s);
     if (valid) epilogue<E>(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
+}
+
+// One workgroup per block of 256 * E elements.
+template <int LEV, bool FP16>
+__global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __restrict__ layer_ptrs,
+                                                          const int64_t* __restrict__ offsets,
+                                                          const uint32_t* __restrict__ tile_layer, int32_t L,
+                                                          int32_t tbl_stride, int32_t tbl_first, int32_t W,
+                                                          int64_t P, float invW, float* __restrict__ grad,
+                                                          int32_t do_sgd, float lr, float mu,
+                                                          float* __restrict__ w, float* __restrict__ v) {
+    tree_layers_block<LEV, FP16>(blockIdx.x, layer_ptrs, offsets, tile_layer, L, tbl_stride, tbl_first, W, P,
+                                 invW, grad, do_sgd, lr, mu, w, v);
+}
+
+// A capped grid (to leave compute units to a concurrent kernel): each
+// workgroup strides over the blocks.
+template <int LEV, bool FP16>
+__global__ __launch_bounds__(kThreads) void k_tree_layers_strided(const uint64_t* __restrict__ layer_ptrs,
+                                                                  const int64_t* __restrict__ offsets,
+                                                                  const uint32_t* __restrict__ tile_layer,
+                                                                  int32_t L, int32_t tbl_stride, int32_t tbl_first,
+                                                                  int32_t W, int64_t P, int64_t n_blocks, float invW,
+                                                                  float* __restrict__ grad, int32_t do_sgd, float lr,
+                                                                  float mu, float* __restrict__ w,
+                                                                  float* __restrict__ v) {
+    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x)
+        tree_layers_block<LEV, FP16>(blk, layer_ptrs, offsets, tile_layer, L, tbl_stride, tbl_first, W, P, invW,
+                                     grad, do_sgd, lr, mu, w, v);
 }
 
 __global__ __launch_bounds__(kThreads) void k_sgd(int64_t P, const float* __restrict__ g,
@@ -336,19 +364,33 @@ hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const g
 }
 
 template <int LEV>
-hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
-                                float* w, float* v, hipStream_t s) {
+hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, int32_t tbl_stride, int32_t tbl_first,
+                                float* grad, const ga_sgd* sgd, float* w, float* v, int32_t max_blocks,
+                                hipStream_t s) {
     const int E = p.dtype == GA_FP16 ? 8 : 4;
     const int64_t threads = (p.P + E - 1) / E;
-    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const int64_t n_blocks = (threads + kThreads - 1) / kThreads;
     const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
-    if (p.dtype == GA_FP16)
-        hipLaunchKernelGGL((k_tree_layers<LEV, true>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets,
-                           p.d_tile_layer, p.L, p.W, p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
-    else
-        hipLaunchKernelGGL((k_tree_layers<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets,
-                           p.d_tile_layer, p.L, p.W, p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    const int do_sgd = sgd ? 1 : 0;
+    if (max_blocks > 0 && max_blocks < n_blocks) {
+        if (p.dtype == GA_FP16)
+            hipLaunchKernelGGL((k_tree_layers_strided<LEV, true>), dim3(max_blocks), dim3(kThreads), 0, s,
+                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P,
+                               n_blocks, invW, grad, do_sgd, lr, mu, w, v);
+        else
+            hipLaunchKernelGGL((k_tree_layers_strided<LEV, false>), dim3(max_blocks), dim3(kThreads), 0, s,
+                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P,
+                               n_blocks, invW, grad, do_sgd, lr, mu, w, v);
+    } else if (p.dtype == GA_FP16) {
+        hipLaunchKernelGGL((k_tree_layers<LEV, true>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P, invW, grad, do_sgd,
+                           lr, mu, w, v);
+    } else {
+        hipLaunchKernelGGL((k_tree_layers<LEV, false>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P, invW, grad, do_sgd,
+                           lr, mu, w, v);
+    }
     return hipGetLastError();
 }
 
@@ -365,9 +407,16 @@ hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_
 
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s) {
+    return launch_tree_layers_sub(p, layer_ptrs, p.L, 0, grad, sgd, w, v, 0, s);
+}
+
+hipError_t launch_tree_layers_sub(const Plan& p, const uint64_t* layer_ptrs, int32_t tbl_stride, int32_t tbl_first,
+                                  float* grad, const ga_sgd* sgd, float* w, float* v, int32_t max_blocks,
+                                  hipStream_t s) {
     if (p.P == 0) return hipSuccess;
-    if (p.W < (1 << 8)) return tree_layers_dispatch<8>(p, layer_ptrs, grad, sgd, w, v, s);
-    return tree_layers_dispatch<11>(p, layer_ptrs, grad, sgd, w, v, s);
+    if (p.W < (1 << 8))
+        return tree_layers_dispatch<8>(p, layer_ptrs, tbl_stride, tbl_first, grad, sgd, w, v, max_blocks, s);
+    return tree_layers_dispatch<11>(p, layer_ptrs, tbl_stride, tbl_first, grad, sgd, w, v, max_blocks, s);
 }
 
 hipError_t launch_sgd(int64_t P, const float* g, float* w, float* v, const ga_sgd* sgd,

@@ -257,6 +257,70 @@ ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const 
 ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, float* d_v,
                                 const ga_sgd* sgd, hipStream_t stream);
 
+/*
+ * Multi-bucket lazy allreduce [GF]: lazy allreduce fuses the layers' gradients
+ * into buckets, and aggregation of a bucket overlaps with the computation of
+ * the layers not yet produced.  A backward pass writes the last layer first,
+ * so buckets are formed from the last layer towards the first.
+ *
+ * ga_bucket_boundaries (host only): cut n_layers layers of layer_numel[l]
+ * elements of elem_bytes (2 or 4) bytes into buckets.  Walking from the last
+ * layer down, a bucket is closed at the start of layer l once it holds at
+ * least bucket_bytes per worker and that start offset (in elements of the
+ * fused row) is a multiple of 8; layer 0 always closes the last bucket.
+ * first_layer[b] (host array of n_layers entries) receives the first layer of
+ * bucket b, bucket 0 being the one holding the last layer; bucket b spans
+ * layers first_layer[b] .. first_layer[b-1]-1 (n_layers-1 for b = 0).
+ * *n_buckets receives the count.  bucket_bytes >= 1; bucket_bytes = 1 makes
+ * one bucket per aligned layer boundary, a huge value one bucket.
+ */
+ga_status ga_bucket_boundaries(int32_t n_layers, const int64_t* layer_numel, int32_t elem_bytes,
+                               int64_t bucket_bytes, int32_t* first_layer, int32_t* n_buckets);
+
+typedef struct ga_buckets ga_buckets;
+
+/*
+ * Bucket schedule of a plan (any plan; only its W, layers and dtype are used):
+ * the buckets of ga_bucket_boundaries, each with a small device offset table of
+ * its own (the only device memory it owns).  Created on the current device.
+ */
+ga_status ga_buckets_create(const ga_plan* plan, int64_t bucket_bytes, ga_buckets** out);
+
+/* Destroy a schedule (NULL is ignored).  No call using it may still be queued. */
+void ga_buckets_destroy(ga_buckets* buckets);
+
+/* Number of buckets (0 for NULL). */
+int32_t ga_buckets_count(const ga_buckets* buckets);
+
+/*
+ * Bucket b's layers (first_layer .. first_layer + n_layers - 1) and its slice
+ * [elem_begin, elem_end) of the fused row, of w, v and g.  Output pointers may
+ * be NULL.  GA_ERR_INVALID for b out of range.
+ */
+ga_status ga_bucket_range(const ga_buckets* buckets, int32_t b, int32_t* first_layer, int32_t* n_layers,
+                          int64_t* elem_begin, int64_t* elem_end);
+
+/*
+ * Aggregate bucket b as ga_tree_reduce_layers does for the whole plan, on
+ * elements [elem_begin, elem_end) only: same tree, mean and fused SGD, so that
+ * reducing every bucket once gives bitwise the result of one
+ * ga_tree_reduce_layers call.
+ *   d_layer_ptrs: the whole plan's W*n_layers table (worker-major); only the
+ *                 bucket's layers are read.
+ *   ready:        NULL, or an event the stream waits for before the launch
+ *                 (recorded by the producer once the bucket's layers are
+ *                 written on every worker).
+ *   d_grad, d_w, d_v: the whole [P] vectors (the bucket's slice is written).
+ *   max_workgroups: 0 for the full grid (one workgroup of 256 threads per
+ *                 2048 binary16 or 1024 binary32 elements); otherwise at most
+ *                 this many workgroups, which stride over the elements, so
+ *                 that a kernel running concurrently (the backward pass) keeps
+ *                 the other compute units.  The result does not depend on it.
+ */
+ga_status ga_bucket_reduce_layers(const ga_buckets* buckets, int32_t b, const uint64_t* d_layer_ptrs,
+                                  hipEvent_t ready, float* d_grad, const ga_sgd* sgd, float* d_w, float* d_v,
+                                  int32_t max_workgroups, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
