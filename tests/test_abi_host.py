@@ -114,3 +114,11 @@ def test_library_does_not_link_the_oracle(ga):
                 assert "oracle" not in text and "workloads" not in text, f
     out = os.popen("ldd %s" % ga.LIB_PATH).read()
     assert "oracle" not in out and "gagen" not in out
+
+
+def test_size_limits_are_inclusive(ga):
+    info = ga.compute_info(ga.MAX_WORKERS, [8 * ga.MAX_CHUNKS], True, 8, 0.1)
+    assert info.n_chunks == ga.MAX_CHUNKS and info.W == ga.MAX_WORKERS
+    with pytest.raises(ga.GAError) as e:
+        ga.compute_info(2, [8 * ga.MAX_CHUNKS + 1], True, 8, 0.1)
+    assert e.value.status == ga.GA_ERR_UNSUPPORTED

@@ -201,3 +201,20 @@ def test_checkpoint_resume_matches_straight_run(ga):
     torch.cuda.synchronize()
     for a, b2 in zip(straight, resumed):
         assert np.array_equal(host(a), host(b2))
+
+
+def test_sparse_maximum_chunk_count(ga):
+    """n_c at the library's limit (65536 chunks of 8 elements, the last one
+    ragged), with the top-k selecting 6554 of them per worker."""
+    n_c = ga.MAX_CHUNKS
+    wl = workloads.custom(2, [8 * (n_c - 1) + 5], True, sigma=1e-3, scale_mode="chunk", scale_log10=(-4.0, 0.0),
+                          chunk=8, rho=0.1)
+    res = run_sparse(ga, wl, steps=2, lazy=True)
+    assert res.keys.shape == (2, n_c)
+
+
+def test_sparse_maximum_worker_count(ga):
+    """W at the library's limit (1024 workers): eleven tree levels."""
+    wl = workloads.custom(ga.MAX_WORKERS, [3000, 77], True, sigma=1e-3, scale_mode="chunk",
+                          scale_log10=(-4.0, 0.0), chunk=256, rho=0.25)
+    run_sparse(ga, wl, steps=2, lazy=True)
