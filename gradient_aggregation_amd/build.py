@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libgradagg.so")
 SOURCES = ["abi.hip", "buckets.hip", "dense.hip", "variants.hip", "norm.hip", "topk.hip", "gather.hip", "pack.hip"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # one rounding per binary32 operation, as the method specifies
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 instructions
@@ -27,13 +27,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _jobs() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("MAX_JOBS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    """Compile every source to an object in parallel, then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(CSRC, s[:-4] + ".o.tmp" + tag) for s in SOURCES]
+
+    def compile_one(i):
+        cmd = [hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+
+    try:
+        with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+            list(ex.map(compile_one, range(len(SOURCES))))
+        tmp = LIB + ".tmp" + tag
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -8,7 +8,7 @@
 
 #include <new>
 
-#include "common.h"
+#include "plan.h"
 
 namespace {
 

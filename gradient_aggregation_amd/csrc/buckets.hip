@@ -12,7 +12,7 @@
 #include <new>
 #include <vector>
 
-#include "common.h"
+#include "plan.h"
 
 struct ga_buckets {
     int32_t W, L, dtype;

@@ -12,7 +12,8 @@
 // U at a time before they are merged, so U 128-bit loads per thread are in
 // flight.  The mean and the SGD update are applied in the same pass: the
 // kernel's HBM traffic is W*P*sizeof(T) + 16*P bytes (w, v read and written).
-#include "common.h"
+#include "device.h"
+#include "plan.h"
 #include "tree.h"
 
 namespace ga {

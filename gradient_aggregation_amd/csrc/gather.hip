@@ -2,7 +2,8 @@
 // workers send, in the fixed binary tree, with the mean and the fused
 // momentum-SGD update.  A worker that did not select a chunk contributes +0
 // without being read.
-#include "common.h"
+#include "device.h"
+#include "plan.h"
 #include "tree.h"
 
 namespace ga {

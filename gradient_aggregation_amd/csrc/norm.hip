@@ -12,7 +12,8 @@
 // per worker-element: 2 B (binary16 gradient) + 4 B (residual read) + 4 B
 // (residual write); in lazy-zero mode the residual of a chunk sent in the
 // previous step is taken as zero and not read.
-#include "common.h"
+#include "device.h"
+#include "plan.h"
 
 namespace ga {
 

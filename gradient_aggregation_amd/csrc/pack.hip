@@ -7,7 +7,8 @@
 // and copies each overlap with 128-bit accesses when the layer tensor and its
 // place in the row are both 16-byte aligned, element by element otherwise.
 // Row padding (elements P..ld-1) is written with zeros.
-#include "common.h"
+#include "device.h"
+#include "plan.h"
 
 namespace ga {
 

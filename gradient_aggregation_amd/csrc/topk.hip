@@ -4,7 +4,8 @@
 // found by a most-significant-digit radix select on the keys' bit patterns
 // (exact integer compares), then masks and the ascending index list follow
 // from workgroup prefix sums in chunk order.
-#include "common.h"
+#include "device.h"
+#include "plan.h"
 
 namespace ga {
 

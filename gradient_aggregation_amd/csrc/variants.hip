@@ -15,7 +15,8 @@
 // receives, and the broadcast result.  The mean and momentum SGD follow as in
 // the dense path.  A thread owns one 128-bit vector of every worker's row
 // (8 binary16 or 4 binary32 elements); loads are issued 16 workers at a time.
-#include "common.h"
+#include "device.h"
+#include "plan.h"
 #include "tree.h"
 
 namespace ga {

@@ -116,3 +116,33 @@ def test_sparse_alexnet128_full_size(ga):
                     r[c * C:min((c + 1) * C, P)] = 0.0
             assert_same_bits(r, r_ref[w, :P], "residual of worker %d" % w)
         log("step %d compared in %.1fs (total %.1fs)" % (step, time.time() - t1, time.time() - t0))
+
+
+@pytest.mark.parametrize("cap", [0, 512])
+def test_buckets_alexnet16_full_size(ga, cap):
+    """Multi-bucket lazy allreduce at full size, as `bench.py --overlap` runs it
+    (4 MiB buckets, layers last-first, each bucket after its event)."""
+    wl = workloads.WORKLOADS["alexnet16"]
+    plan = ga.Plan(wl.W, wl.numels, wl.fp16)
+    bk = ga.Buckets(plan, 4 << 20)
+    assert bk.count == 5
+    w_ref = workloads.weights(wl)
+    v_ref = np.zeros(wl.P, np.float32)
+    wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
+    side = torch.cuda.Stream()
+    for step in (1, 2):
+        t0 = time.time()
+        b = workloads.grad_bucket(wl, step, plan.ld)
+        src, ptrs = device_layers(b[:, :wl.P], wl.numels)
+        g_ref = oracle.dense_step(b, wl.P, wl.fp16, wl.lr, wl.mu, w_ref, v_ref)
+        del b
+        ready = torch.cuda.Event()
+        ready.record()
+        with torch.cuda.stream(side):
+            for i in range(bk.count):
+                bk.reduce_layers(i, ptrs, ready, None, wd, vd, wl.lr, wl.mu, max_workgroups=cap)
+        torch.cuda.synchronize()
+        del src
+        assert_same_bits(host(wd), w_ref, "w")
+        assert_same_bits(host(vd), v_ref, "v")
+        log("alexnet16 buckets (cap %d) step %d ok in %.1fs" % (cap, step, time.time() - t0))
