@@ -306,6 +306,9 @@ def main():
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "traffic_source": None if traffic is None else traffic["summary"],
             "bytes_per_launch": dom_bytes, "mean_launch_ms": round(dom_ms, 4),
+            # the same chip's plain-copy rate in this run (the fusion copy of the
+            # per-layer tensors, below): the measured ceiling for mixed read/write
+            "vs_plain_copy": round(achieved / pack["GBps"], 3) if pack.get("GBps") else None,
         },
         "pack": pack,
         "ms_per_step_with_pack": round(ms_step + pack["mean_ms"], 4),

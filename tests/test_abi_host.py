@@ -122,3 +122,14 @@ def test_size_limits_are_inclusive(ga):
     with pytest.raises(ga.GAError) as e:
         ga.compute_info(2, [8 * ga.MAX_CHUNKS + 1], True, 8, 0.1)
     assert e.value.status == ga.GA_ERR_UNSUPPORTED
+
+
+def test_header_is_plain_c_and_client_links(ga):
+    """include/gradagg.h compiles as C11 with gcc and a C program links against
+    the library (the client itself runs in the GPU tests)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("c_build", os.path.join(ROOT, "tests", "c", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    exe = mod.build()
+    assert os.path.exists(exe)
