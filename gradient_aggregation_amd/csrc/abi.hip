@@ -162,7 +162,8 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
     const int64_t vec = grad_dtype == GA_FP16 ? 8 : 4;
     p->tile_elems = 64 * vec;
     const int64_t n_tiles = (info.P + p->tile_elems - 1) / p->tile_elems;
-    uint32_t* h_tiles = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)n_tiles);
+    p->n_tiles = n_tiles;
+    uint32_t* h_tiles = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(2 * n_tiles));
     if (!h_tiles) {
         free(p->h_offsets);
         delete p;
@@ -176,15 +177,23 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
             const bool whole = p->h_offsets[l + 1] >= e0 + p->tile_elems && p->h_offsets[l] % vec == 0;
             h_tiles[t] = (uint32_t)l | (whole ? 0x80000000u : 0u);
         }
+        uint32_t* order = h_tiles + n_tiles;
+        int64_t j = 0;
+        for (int64_t t = 0; t < n_tiles; ++t)
+            if (!(h_tiles[t] >> 31)) order[j++] = (uint32_t)t;
+        for (int64_t t = 0; t < n_tiles; ++t)
+            if (h_tiles[t] >> 31) order[j++] = (uint32_t)t;
     }
     p->d_tile_layer = nullptr;
+    p->d_tile_order = nullptr;
     hipError_t e = hipGetDevice(&p->device);
     if (e == hipSuccess) e = hipMalloc((void**)&p->d_offsets, sizeof(int64_t) * (size_t)(n_layers + 1));
     if (e == hipSuccess)
         e = hipMemcpy(p->d_offsets, p->h_offsets, sizeof(int64_t) * (size_t)(n_layers + 1), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMalloc((void**)&p->d_tile_layer, sizeof(uint32_t) * (size_t)n_tiles);
+    if (e == hipSuccess) e = hipMalloc((void**)&p->d_tile_layer, sizeof(uint32_t) * (size_t)(2 * n_tiles));
     if (e == hipSuccess)
-        e = hipMemcpy(p->d_tile_layer, h_tiles, sizeof(uint32_t) * (size_t)n_tiles, hipMemcpyHostToDevice);
+        e = hipMemcpy(p->d_tile_layer, h_tiles, sizeof(uint32_t) * (size_t)(2 * n_tiles), hipMemcpyHostToDevice);
+    if (e == hipSuccess) p->d_tile_order = p->d_tile_layer + n_tiles;
     free(h_tiles);
     if (e != hipSuccess) {
         if (p->d_offsets) (void)hipFree(p->d_offsets);

@@ -57,10 +57,31 @@ struct LeafVec<true> {
     static __device__ __forceinline__ void widen(const raw& r, float (&f)[E]) { widen8(r, f); }
 };
 
-template <int E>
+// The thread's w and v, loaded before its leaves so that their latency
+// overlaps the leaves' instead of following the tree (full vectors only; a
+// ragged tail loads them in the epilogue).  PF = false (the 11-level trees,
+// whose registers are needed for the tree) loads them in the epilogue.
+template <int E, bool PF>
+struct SgdState {
+    float4 w[E / 4], v[E / 4];
+};
+
+template <int E, bool PF>
+__device__ __forceinline__ void prefetch_state(int64_t i0, int64_t P, bool do_sgd, const float* __restrict__ w,
+                                               const float* __restrict__ v, SgdState<E, PF>& st) {
+    if (PF && do_sgd && i0 + E <= P) {
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+            st.w[q] = *reinterpret_cast<const float4*>(w + i0 + 4 * q);
+            st.v[q] = *reinterpret_cast<const float4*>(v + i0 + 4 * q);
+        }
+    }
+}
+
+template <int E, bool PF>
 __device__ __forceinline__ void epilogue(const float (&s)[E], int64_t i0, int64_t P, float invW,
                                          float* __restrict__ grad, bool do_sgd, float lr, float mu,
-                                         float* __restrict__ w, float* __restrict__ v) {
+                                         float* __restrict__ w, float* __restrict__ v, SgdState<E, PF>& st) {
     float g[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) g[e] = s[e] * invW;
@@ -72,15 +93,19 @@ __device__ __forceinline__ void epilogue(const float (&s)[E], int64_t i0, int64_
         }
         if (do_sgd) {
 #pragma unroll
-            for (int e = 0; e < E; e += 4) {
-                float4 wv = *reinterpret_cast<const float4*>(w + i0 + e);
-                float4 vv = *reinterpret_cast<const float4*>(v + i0 + e);
-                sgd_update(g[e + 0], lr, mu, wv.x, vv.x);
-                sgd_update(g[e + 1], lr, mu, wv.y, vv.y);
-                sgd_update(g[e + 2], lr, mu, wv.z, vv.z);
-                sgd_update(g[e + 3], lr, mu, wv.w, vv.w);
-                *reinterpret_cast<float4*>(w + i0 + e) = wv;
-                *reinterpret_cast<float4*>(v + i0 + e) = vv;
+            for (int q = 0; q < E / 4; ++q) {
+                if (!PF) {
+                    st.w[q] = *reinterpret_cast<const float4*>(w + i0 + 4 * q);
+                    st.v[q] = *reinterpret_cast<const float4*>(v + i0 + 4 * q);
+                }
+                float4& wv = st.w[q];
+                float4& vv = st.v[q];
+                sgd_update(g[4 * q + 0], lr, mu, wv.x, vv.x);
+                sgd_update(g[4 * q + 1], lr, mu, wv.y, vv.y);
+                sgd_update(g[4 * q + 2], lr, mu, wv.z, vv.z);
+                sgd_update(g[4 * q + 3], lr, mu, wv.w, vv.w);
+                *reinterpret_cast<float4*>(w + i0 + 4 * q) = wv;
+                *reinterpret_cast<float4*>(v + i0 + 4 * q) = vv;
             }
         }
     } else {
@@ -112,6 +137,8 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
     if (i0 >= P) return;
     const int64_t row_bytes = ld * (FP16 ? 2 : 4);
     const char* base = static_cast<const char*>(bucket) + i0 * (FP16 ? 2 : 4);
+    SgdState<E, (LEV <= 8)> st;
+    prefetch_state(i0, P, do_sgd != 0, w, v, st);
 
     TreeAcc<LEV, E> tree;
     uint32_t cnt = 0;
@@ -132,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
     }
     float s[E];
     tree.result((uint32_t)W, s);
-    epilogue<E>(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
+    epilogue(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v, st);
 }
 
 // Zero-copy lazy-allreduce fusion for the dense path: the leaves are read
@@ -144,7 +171,9 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
 template <int LEV, bool FP16>
 __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* __restrict__ layer_ptrs,
                                                   const int64_t* __restrict__ offsets,
-                                                  const uint32_t* __restrict__ tile_layer, int32_t L,
+                                                  const uint32_t* __restrict__ tile_layer,
+                                                  const uint32_t* __restrict__ tile_order, int64_t n_tiles,
+                                                  int32_t L,
                                                   int32_t tbl_stride, int32_t tbl_first, int32_t W, int64_t P,
                                                   float invW, float* __restrict__ grad, int32_t do_sgd, float lr,
                                                   float mu, float* __restrict__ w, float* __restrict__ v) {
@@ -153,11 +182,15 @@ __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* _
     constexpr int kEsz = FP16 ? 2 : 4;
     using raw = typename LV::raw;
     const int lane = threadIdx.x & 63;
-    const int64_t wave_base =
-        (blk * kThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
-    if (wave_base >= P) return;
+    // the wavefront's tile, in the plan's order (straddling tiles first)
+    const int64_t gw = blk * (kThreads / 64) + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (gw >= n_tiles) return;
+    const uint32_t tile = tile_order[gw];
+    const int64_t wave_base = (int64_t)tile * (64 * E);
     const int64_t i0 = wave_base + (int64_t)lane * E;
     const bool valid = i0 < P;
+    SgdState<E, (LEV <= 8)> st;
+    prefetch_state(i0, P, do_sgd != 0, w, v, st);
 
     auto layer_of = [&](int64_t i) {
         int32_t lo = 0, hi = L;
@@ -169,7 +202,7 @@ __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* _
         return lo;
     };
     // The plan's tile table gives the wavefront's layer in one scalar load.
-    const uint32_t tinfo = tile_layer[wave_base / (64 * E)];
+    const uint32_t tinfo = tile_layer[tile];
     const int32_t l0 = (int32_t)(tinfo & 0x7fffffffu);
     const int64_t off0 = offsets[l0];
     // Fast path: the wavefront's 64*E elements all exist, lie in layer l0 at an
@@ -290,20 +323,22 @@ __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* _
     }
     float s[E];
     tree.result((uint32_t)W, s);
-    if (valid) epilogue<E>(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v);
+    if (valid) epilogue(s, i0, P, invW, grad, do_sgd != 0, lr, mu, w, v, st);
 }
 
 // One workgroup per block of 256 * E elements.
 template <int LEV, bool FP16>
 __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __restrict__ layer_ptrs,
                                                           const int64_t* __restrict__ offsets,
-                                                          const uint32_t* __restrict__ tile_layer, int32_t L,
-                                                          int32_t tbl_stride, int32_t tbl_first, int32_t W,
-                                                          int64_t P, float invW, float* __restrict__ grad,
-                                                          int32_t do_sgd, float lr, float mu,
-                                                          float* __restrict__ w, float* __restrict__ v) {
-    tree_layers_block<LEV, FP16>(blockIdx.x, layer_ptrs, offsets, tile_layer, L, tbl_stride, tbl_first, W, P,
-                                 invW, grad, do_sgd, lr, mu, w, v);
+                                                          const uint32_t* __restrict__ tile_layer,
+                                                          const uint32_t* __restrict__ tile_order,
+                                                          int64_t n_tiles, int32_t L, int32_t tbl_stride,
+                                                          int32_t tbl_first, int32_t W, int64_t P, float invW,
+                                                          float* __restrict__ grad, int32_t do_sgd, float lr,
+                                                          float mu, float* __restrict__ w,
+                                                          float* __restrict__ v) {
+    tree_layers_block<LEV, FP16>(blockIdx.x, layer_ptrs, offsets, tile_layer, tile_order, n_tiles, L, tbl_stride,
+                                 tbl_first, W, P, invW, grad, do_sgd, lr, mu, w, v);
 }
 
 // A capped grid (to leave compute units to a concurrent kernel): each
@@ -312,14 +347,16 @@ template <int LEV, bool FP16>
 __global__ __launch_bounds__(kThreads) void k_tree_layers_strided(const uint64_t* __restrict__ layer_ptrs,
                                                                   const int64_t* __restrict__ offsets,
                                                                   const uint32_t* __restrict__ tile_layer,
-                                                                  int32_t L, int32_t tbl_stride, int32_t tbl_first,
-                                                                  int32_t W, int64_t P, int64_t n_blocks, float invW,
+                                                                  const uint32_t* __restrict__ tile_order,
+                                                                  int64_t n_tiles, int32_t L, int32_t tbl_stride,
+                                                                  int32_t tbl_first, int32_t W, int64_t P,
+                                                                  int64_t n_blocks, float invW,
                                                                   float* __restrict__ grad, int32_t do_sgd, float lr,
                                                                   float mu, float* __restrict__ w,
                                                                   float* __restrict__ v) {
     for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x)
-        tree_layers_block<LEV, FP16>(blk, layer_ptrs, offsets, tile_layer, L, tbl_stride, tbl_first, W, P, invW,
-                                     grad, do_sgd, lr, mu, w, v);
+        tree_layers_block<LEV, FP16>(blk, layer_ptrs, offsets, tile_layer, tile_order, n_tiles, L, tbl_stride,
+                                     tbl_first, W, P, invW, grad, do_sgd, lr, mu, w, v);
 }
 
 __global__ __launch_bounds__(kThreads) void k_sgd(int64_t P, const float* __restrict__ g,
@@ -377,20 +414,20 @@ hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, int32
     if (max_blocks > 0 && max_blocks < n_blocks) {
         if (p.dtype == GA_FP16)
             hipLaunchKernelGGL((k_tree_layers_strided<LEV, true>), dim3(max_blocks), dim3(kThreads), 0, s,
-                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P,
-                               n_blocks, invW, grad, do_sgd, lr, mu, w, v);
+                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride,
+                               tbl_first, p.W, p.P, n_blocks, invW, grad, do_sgd, lr, mu, w, v);
         else
             hipLaunchKernelGGL((k_tree_layers_strided<LEV, false>), dim3(max_blocks), dim3(kThreads), 0, s,
-                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P,
-                               n_blocks, invW, grad, do_sgd, lr, mu, w, v);
+                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride,
+                               tbl_first, p.W, p.P, n_blocks, invW, grad, do_sgd, lr, mu, w, v);
     } else if (p.dtype == GA_FP16) {
         hipLaunchKernelGGL((k_tree_layers<LEV, true>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P, invW, grad, do_sgd,
-                           lr, mu, w, v);
+                           p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride, tbl_first, p.W,
+                           p.P, invW, grad, do_sgd, lr, mu, w, v);
     } else {
         hipLaunchKernelGGL((k_tree_layers<LEV, false>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.L, tbl_stride, tbl_first, p.W, p.P, invW, grad, do_sgd,
-                           lr, mu, w, v);
+                           p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride, tbl_first, p.W,
+                           p.P, invW, grad, do_sgd, lr, mu, w, v);
     }
     return hipGetLastError();
 }

@@ -20,7 +20,12 @@ struct Plan {
     // the tile's first element, bit 31 set when the whole tile lies in that
     // layer at a vector-aligned offset.
     uint32_t* d_tile_layer;
-    int64_t tile_elems;
+    // The order in which the wavefronts take the tiles: tiles that straddle a
+    // layer boundary (or start at an unaligned offset) first, then the rest
+    // in ascending order, so that the slow ones do not form the kernel's tail.
+    // Same allocation as d_tile_layer (its second half).
+    uint32_t* d_tile_order;
+    int64_t tile_elems, n_tiles;
 };
 
 // ---- ABI error reporting (defined in abi.hip) ---------------------------
