@@ -279,9 +279,11 @@ def main():
     value = b_alg / (ms_step * 1e-3) / 1e9
     dom_ms = per_kernel[dom]["mean_ms"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = None if variant else measured_traffic(
-        args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
-        "k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree")
+    dom_kernel = ("k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree") if not variant \
+        else "k_variant_" + ("tree" if args.order == "tree" else "seq")
+    traffic_key = dom_kernel if not variant else "%s_order_%s_wire_%s" % (dom_kernel, args.order, args.wire)
+    traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
+                               traffic_key)
 
     result = {
         "metric": METRIC,
@@ -316,8 +318,7 @@ def main():
         "kernels": per_kernel,
         "first_step_ms": first_step if sparse else None,
         "roofline": {
-            "kernel": ("k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree") if not variant
-                      else "k_variant_" + ("tree" if args.order == "tree" else "seq"),
+            "kernel": dom_kernel,
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
