@@ -277,6 +277,17 @@ def main():
         b_alg = W * P * b_in + 16 * P
         dom, dom_bytes = "tree_sgd", b_alg
     value = b_alg / (ms_step * 1e-3) / 1e9
+    # algorithmic bytes and rate of every kernel of the step
+    if sparse:
+        kbytes = {"chunk_norm": W * P * (b_in + 4 + 4),
+                  "topk": W * plan.n_chunks * 8,
+                  "gather_sgd": W * plan.k * plan.chunk * 4 + 16 * P}
+    else:
+        kbytes = {"tree_sgd": b_alg}
+    for nm, nb in kbytes.items():
+        per_kernel[nm]["bytes_alg"] = nb
+        per_kernel[nm]["GBps_alg"] = round(nb / (per_kernel[nm]["mean_ms"] * 1e-3) / 1e9, 1)
+        per_kernel[nm]["frac_hbm_peak"] = round(per_kernel[nm]["GBps_alg"] / HBM_PEAK_GBPS, 4)
     dom_ms = per_kernel[dom]["mean_ms"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     dom_kernel = ("k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree") if not variant \
