@@ -101,9 +101,17 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_wave(
     uint64_t mb[kGroups > 0 ? kGroups : 1];
     bool any = false;
     if (kGroups > 0) {
+        // every group's mask word is requested before the first ballot, so
+        // the (at most four) loads are in flight together
+        uint32_t word[kGroups > 0 ? kGroups : 1];
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi) {
-            mb[gi] = gi * 64 < W ? bitmap(gi * 64) : 0ull;
+            const int32_t wk = gi * 64 + lane;
+            word[gi] = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
+        }
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+            mb[gi] = __ballot((word[gi] & cb) != 0u);
             any |= mb[gi] != 0ull;
         }
     } else {
