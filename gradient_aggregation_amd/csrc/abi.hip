@@ -280,7 +280,8 @@ ga_status ga_reduce_variant(const ga_plan* plan, const void* d_bucket, ga_order 
         return fail(GA_ERR_INVALID, "unknown order %d", (int)order);
     if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
     if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
-    if (!aligned16(d_bucket)) return fail(GA_ERR_ALIGN, "bucket not 16-byte aligned");
+    if (!aligned16(d_bucket) || (d_grad && !aligned16(d_grad)) || (sgd && (!aligned16(d_w) || !aligned16(d_v))))
+        return fail(GA_ERR_ALIGN, "device buffers must be 16-byte aligned");
     const ga::Plan* p = as_plan(plan);
     ga_status st = check_device(p);
     if (st != GA_OK) return st;

@@ -146,6 +146,14 @@ def test_device_argument_errors(ga):
         plan.chunk_norm(b, torch.zeros(4 * plan.ld, device="cuda"), torch.zeros(4, dtype=torch.float64,
                                                                                  device="cuda"))
     assert e.value.status == ga.GA_ERR_INVALID
+    # every entry point that writes g, w, v with 128-bit stores rejects a misaligned one before launching
+    wv = torch.zeros(plan.P + 1, dtype=torch.float32, device="cuda")
+    for call in (lambda: plan.reduce_variant(b[:4 * plan.ld], "ring", False, g[1:]),
+                 lambda: plan.reduce_variant(b[:4 * plan.ld], "server", True, None, wv[1:], wv[:plan.P], 0.1, 0.9),
+                 lambda: plan.tree_reduce(b[:4 * plan.ld], None, wv[:plan.P], wv[1:], 0.1, 0.9)):
+        with pytest.raises(ga.GAError) as e:
+            call()
+        assert e.value.status == ga.GA_ERR_ALIGN
     with pytest.raises(ValueError):
         plan.tree_reduce(b[:4 * plan.ld].cpu(), g)
     with pytest.raises(ValueError):
