@@ -4,14 +4,17 @@
 Default workload: AlexNet-shaped, W=128 workers x P=60,965,224 parameters,
 binary16 gradients, coarse-grained sparse communication with 32768-element
 chunks keeping 10% of them per worker (k=187 of 1861), the residual carried in
-lazy-zero mode, and momentum SGD on binary32 master weights.
+lazy-zero mode (deferred form by default: a chunk sent in the previous step
+stores no a, and the gather reads its gradient), and momentum SGD on binary32
+master weights.
 
 One step = lazy-allreduce fusion of the W*16 per-layer gradient tensors read
 with zero copy through the layer table, together with the chunk norms and the
 residual (k_chunk_norm), top-k chunk selection (k_topk), and the gather-reduce
-of the selected chunks fused with the mean and the SGD update (k_gather), over
-one batch of gradients already resident in HBM (three gradient batches are
-cycled so that consecutive steps see fresh inputs).
+of the selected chunks fused with the mean and the SGD update (k_gather_defer,
+or k_gather_wave with --residual lazy), over one batch of gradients already
+resident in HBM (three gradient batches are cycled so that consecutive steps
+see fresh inputs).
 
 Prints one JSON line:
   value            algorithmic GB/s of the whole step, B_alg / step time, where
@@ -20,7 +23,7 @@ Prints one JSON line:
   roofline         the dominant kernel (k_chunk_norm): 10*W*P bytes per launch
                    over its mean launch time from HIP events on its stream,
                    against the 8 TB/s HBM peak
-  cpu_baseline     the oracle timed on the host cores on a sample of workers
+  cpu_baseline     the oracle timed on the host cores, one whole step
 """
 from __future__ import annotations
 
@@ -54,6 +57,9 @@ def parse():
     ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
     ap.add_argument("--source", choices=["layers", "bucket"], default="layers",
                     help="gradients as per-layer tensors fused with zero copy (default) or a packed bucket")
+    ap.add_argument("--residual", choices=["deferred", "lazy"], default="deferred",
+                    help="sparse workload: lazy-zero residual with one mask buffer, or its deferred form (chunks "
+                         "sent in the previous step store no a; the gather reads their gradient)")
     ap.add_argument("--order", choices=["tree", "server", "ring"], default="tree",
                     help="dense workloads: summation order (parameter server, ring) for comparison")
     ap.add_argument("--wire", choices=["f32", "f16"], default="f32",
@@ -200,11 +206,15 @@ def main():
     gen_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
+    defer = False
     if sparse:
         rd = plan.empty_residual()
         keys = plan.empty_keys()
         idx = torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda")
         mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
+        # deferred mode: two mask buffers swap roles (previous / current step)
+        masks = [mask, torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")]
+        defer = args.residual == "deferred" and layers_src and plan.chunk % 256 == 0
         names = ["chunk_norm", "topk", "gather_sgd"]
     else:
         names = ["tree_sgd"]
@@ -217,7 +227,18 @@ def main():
         e = ev[t]
         if rec:
             e[0].record(stream)
-        if sparse:
+        if sparse and defer:
+            prev, cur = masks[t % 2], masks[(t + 1) % 2]
+            plan.chunk_norm_layers_defer(b, rd, keys, prev)
+            if rec:
+                e[1].record(stream)
+            plan.chunk_topk(keys, idx, cur)
+            if rec:
+                e[2].record(stream)
+            plan.sparse_gather_reduce_layers_defer(b, rd, prev, cur, None, wd, vd, wl.lr, wl.mu)
+            if rec:
+                e[3].record(stream)
+        elif sparse:
             if layers_src:
                 plan.chunk_norm_layers(b, rd, keys, mask if t > 0 else None)
             else:
@@ -293,6 +314,8 @@ def main():
     dom_kernel = ("k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree") if not variant \
         else "k_variant_" + ("tree" if args.order == "tree" else "seq")
     traffic_key = dom_kernel if not variant else "%s_order_%s_wire_%s" % (dom_kernel, args.order, args.wire)
+    if defer:
+        traffic_key = dom_kernel + "_deferred"
     traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
                                traffic_key)
 
@@ -315,7 +338,8 @@ def main():
             "accumulate": "f32 fixed binary tree", "keys": "f64" if sparse else None,
             "chunk": plan.chunk or None, "keep_ratio": wl.rho if sparse else None,
             "k": plan.k if sparse else None, "n_chunks": plan.n_chunks if sparse else None,
-            "residual_mode": "lazy-zero" if sparse else None, "gradient_batches": nb,
+            "residual_mode": ("deferred lazy-zero" if defer else "lazy-zero") if sparse else None,
+            "gradient_batches": nb,
             "fusion": "zero-copy read of %d per-layer tensors" % (W * len(wl.numels)) if layers_src
                       else "pre-packed bucket",
             "order": args.order, "wire": args.wire,
@@ -333,6 +357,9 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
+            # the bytes the kernel moves (counters) over its time, beside the
+            # algorithmic figure above
+            "moved_GBps": None if traffic is None else round(traffic["bytes_per_launch"] / (dom_ms * 1e-3) / 1e9, 1),
             "traffic_source": None if traffic is None else traffic["summary"],
             "bytes_per_launch": dom_bytes, "mean_launch_ms": round(dom_ms, 4),
             # the same chip's plain-copy rate in this run (the fusion copy of the

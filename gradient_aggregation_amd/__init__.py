@@ -90,6 +90,11 @@ def lib() -> ctypes.CDLL:
                                               _VP]
         L.ga_sgd_momentum_apply.restype = st
         L.ga_sgd_momentum_apply.argtypes = [ctypes.c_int64, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP]
+        L.ga_chunk_norm_layers_defer.restype = st
+        L.ga_chunk_norm_layers_defer.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_sparse_gather_reduce_layers_defer.restype = st
+        L.ga_sparse_gather_reduce_layers_defer.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP,
+                                                           _VP, _VP]
         L.ga_bucket_boundaries.restype = st
         L.ga_bucket_boundaries.argtypes = [ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP]
         L.ga_buckets_create.restype = st
@@ -274,6 +279,31 @@ class Plan:
                                           _dev(resid, torch.float32, self.W * self.ld, "resid"),
                                           _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
                                           _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
+
+    def chunk_norm_layers_defer(self, layer_ptrs, resid, keys, prev_mask) -> None:
+        """Deferred-residual chunk norms: chunks set in prev_mask do not store a."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        _check(lib().ga_chunk_norm_layers_defer(
+            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
+
+    def sparse_gather_reduce_layers_defer(self, layer_ptrs, resid, prev_mask, sel_mask, grad=None, w=None, v=None,
+                                          lr: Optional[float] = None, mu: Optional[float] = None) -> None:
+        """Deferred-residual gather-reduce (reads the gradient tensors for
+        chunks sent now and in the previous step)."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_sparse_gather_reduce_layers_defer(
+            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
+            _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
+            _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
 
     def chunk_norm(self, bucket, resid, keys, prev_mask=None) -> None:
         torch = _torch()

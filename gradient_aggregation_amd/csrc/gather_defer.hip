@@ -1,0 +1,329 @@
+// Coarse-grained sparse communication, part 3, deferred-residual form
+// (GradientFlow, arXiv abstract: only the important chunks are sent; the rest
+// stay in the worker's residual).
+//
+// In lazy-zero mode a chunk that a worker sent in the previous step has a zero
+// residual, so its a is just the worker's widened gradient.  The deferred norm
+// pass does not store that a.  This gather then
+//   - takes the leaf of a chunk sent now and in the previous step from the
+//     gradient tensors (2 bytes per binary16 element instead of 4),
+//   - writes the residual of a chunk sent in the previous step but not now
+//     (the widened gradient), so that afterwards the residual buffer holds
+//     exactly what the non-deferred lazy mode leaves,
+//   - and otherwise reduces like k_gather_wave: every worker pushes its leaf or
+//     +0 into the fixed tree, then the mean and the fused SGD update.
+// A wavefront covers 256 consecutive elements of one chunk (C is a multiple of
+// 256), so the two mask bits of a worker are wavefront-uniform.
+#include "device.h"
+#include "plan.h"
+#include "tree.h"
+
+namespace ga {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 16;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Worker wk's 4 gradient elements at i0 (i0 % 4 == 0), element by element:
+// for tensors that are not aligned for a vector load, or a wavefront that
+// straddles layers (la: the lane's layer, ea: its end).  Widened, plus +0.
+template <bool FP16>
+__device__ __noinline__ float4 grad4_slow(const uint64_t* __restrict__ layer_ptrs,
+                                          const int64_t* __restrict__ offsets, int32_t L, int32_t wk,
+                                          int32_t la, int64_t ea, int64_t i0, int64_t P) {
+    float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + e;
+        if (i < P) {
+            int32_t l = la;
+            if (i >= ea) {
+                l = la + 1;
+                while (offsets[l + 1] <= i) ++l;
+            }
+            const uint64_t a = layer_ptrs[(int64_t)wk * L + l];
+            const int64_t j = i - offsets[l];
+            f[e] = FP16 ? widen1(as_global<uint16_t>(a)[j]) : as_global<float>(a)[j];
+        }
+    }
+    return make_float4(f[0] + 0.f, f[1] + 0.f, f[2] + 0.f, f[3] + 0.f);
+}
+
+// A leaf as loaded: 4 binary32 residual values; or 4 gradient elements
+// (binary16 in the first two words, or binary32) to widen and add +0 to (the
+// residual of a chunk sent in the previous step is +0, and a = leaf + residual
+// maps a -0 leaf to +0 exactly as the non-deferred pass does); or values the
+// element-by-element path already produced.
+enum LeafKind { kResid = 0, kGradVec = 1, kReady = 2 };
+
+template <bool FP16>
+__device__ __forceinline__ float4 decode_leaf(const v4u& x, int kind) {
+    if (kind == kGradVec) {
+        if (FP16)
+            return make_float4(widen1((uint16_t)(x.x & 0xffffu)) + 0.f, widen1((uint16_t)(x.x >> 16)) + 0.f,
+                               widen1((uint16_t)(x.y & 0xffffu)) + 0.f, widen1((uint16_t)(x.y >> 16)) + 0.f);
+        return make_float4(__uint_as_float(x.x) + 0.f, __uint_as_float(x.y) + 0.f, __uint_as_float(x.z) + 0.f,
+                           __uint_as_float(x.w) + 0.f);
+    }
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+}
+
+// Worker wk's gradient vector at the lane's elements: with a vector load from
+// the address held by lane b of `mine` (vec), else element by element.
+template <bool FP16>
+__device__ __forceinline__ v4u load_grad(bool vec, uint64_t mine, int b, int64_t byte_off,
+                                         const uint64_t* __restrict__ layer_ptrs,
+                                         const int64_t* __restrict__ offsets, int32_t L, int32_t wk, int32_t la,
+                                         int64_t ea, int64_t i0, int64_t P) {
+    if (vec) {
+        const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(mine >> 32), b) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, b);
+        const uint64_t addr = base + (uint64_t)byte_off;
+        if (FP16) {
+            const v2u x = *as_global<v2u>(addr);
+            return v4u{x.x, x.y, 0u, 0u};
+        }
+        return *as_global<v4u>(addr);
+    }
+    const float4 f = grad4_slow<FP16>(layer_ptrs, offsets, L, wk, la, ea, i0, P);
+    return v4u{__float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(f.z), __float_as_uint(f.w)};
+}
+
+__device__ __forceinline__ uint64_t pick(int gi, uint64_t a0, uint64_t a1, uint64_t a2, uint64_t a3) {
+    return gi == 0 ? a0 : gi == 1 ? a1 : gi == 2 ? a2 : a3;
+}
+
+template <int LEV, bool FP16>
+__global__ __launch_bounds__(kThreads) void k_gather_defer(
+    const uint64_t* __restrict__ layer_ptrs, const int64_t* __restrict__ offsets,
+    const uint32_t* __restrict__ tile_layer, int64_t tile_elems, int32_t L, float* __restrict__ resid,
+    int64_t ld, int32_t W, int64_t P, int64_t C, const uint32_t* __restrict__ prev_mask,
+    const uint32_t* __restrict__ sel_mask, int32_t mw, float invW, float* __restrict__ grad, int32_t do_sgd,
+    float lr, float mu, float* __restrict__ w, float* __restrict__ v) {
+    static_assert(LEV <= 8, "the deferred gather keeps at most four 64-worker groups in registers");
+    constexpr int E = 4;
+    constexpr int64_t kEsz = FP16 ? 2 : 4;
+    constexpr uint64_t kAlignMask = FP16 ? 7ull : 15ull;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base =
+        ((int64_t)blockIdx.x * kThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
+    if (wave_base >= P) return;
+    const int64_t i0 = wave_base + (int64_t)lane * E;
+    const bool valid = i0 < P;
+    const bool full = i0 + E <= P;
+    const int32_t c = (int32_t)(wave_base / C);
+    const int32_t cw = c >> 5;
+    const uint32_t cb = 1u << (c & 31);
+
+    // Both bitmaps of the (at most four) 64-worker groups, every mask word in
+    // flight together: sent now (mc), sent in the previous step (mp).
+    uint32_t sw[4], pw[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        const int32_t wk = gi * 64 + lane;
+        sw[gi] = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
+        pw[gi] = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
+    }
+    const uint64_t mc0 = __ballot((sw[0] & cb) != 0u), mc1 = __ballot((sw[1] & cb) != 0u);
+    const uint64_t mc2 = __ballot((sw[2] & cb) != 0u), mc3 = __ballot((sw[3] & cb) != 0u);
+    const uint64_t mp0 = __ballot((pw[0] & cb) != 0u), mp1 = __ballot((pw[1] & cb) != 0u);
+    const uint64_t mp2 = __ballot((pw[2] & cb) != 0u), mp3 = __ballot((pw[3] & cb) != 0u);
+    const bool any_sent = (mc0 | mc1 | mc2 | mc3) != 0ull;
+    const bool any_prev = (mp0 | mp1 | mp2 | mp3) != 0ull;
+
+    float4 wv = make_float4(0.f, 0.f, 0.f, 0.f), vv = wv;
+    if (do_sgd && full) {
+        wv = *reinterpret_cast<const float4*>(w + i0);
+        vv = *reinterpret_cast<const float4*>(v + i0);
+    }
+
+    // Where the gradient elements live: the plan's tile table gives the layer
+    // of the wavefront's tile and whether the tile lies in it at an aligned
+    // offset (whole); otherwise each lane finds its layer.
+    bool whole = false;
+    int32_t l0 = 0, la = 0;
+    int64_t off0 = 0, ea = 0;
+    // lane l holds worker (64 gi + l)'s tensor address for layer l0 (whole
+    // tiles), and vN says every address of group N allows the vector load
+    uint64_t p0 = 0ull, p1 = 0ull, p2 = 0ull, p3 = 0ull;
+    bool v0 = false, v1 = false, v2 = false, v3 = false;
+    if (any_prev) {
+        const uint32_t tinfo = tile_layer[wave_base / tile_elems];
+        l0 = (int32_t)(tinfo & 0x7fffffffu);
+        off0 = offsets[l0];
+        whole = (tinfo >> 31) != 0u;
+        if (whole) {
+            p0 = lane < W ? layer_ptrs[(int64_t)lane * L + l0] : 0ull;
+            p1 = 64 + lane < W ? layer_ptrs[(int64_t)(64 + lane) * L + l0] : 0ull;
+            p2 = 128 + lane < W ? layer_ptrs[(int64_t)(128 + lane) * L + l0] : 0ull;
+            p3 = 192 + lane < W ? layer_ptrs[(int64_t)(192 + lane) * L + l0] : 0ull;
+            v0 = __ballot((p0 & kAlignMask) != 0ull) == 0ull;
+            v1 = __ballot((p1 & kAlignMask) != 0ull) == 0ull;
+            v2 = __ballot((p2 & kAlignMask) != 0ull) == 0ull;
+            v3 = __ballot((p3 & kAlignMask) != 0ull) == 0ull;
+        } else if (valid) {
+            int32_t lo = l0, hi = L;   // the lane's layer is l0 or a later one
+            while (lo < hi) {
+                const int32_t mid = (lo + hi) >> 1;
+                if (offsets[mid + 1] <= i0) lo = mid + 1;
+                else hi = mid;
+            }
+            la = lo;
+            ea = offsets[lo + 1];
+        }
+        if (whole) {
+            la = l0;
+            ea = offsets[l0 + 1];
+        }
+    }
+    const int64_t byte_off = (i0 - off0) * kEsz;
+
+    float s[E] = {0.f, 0.f, 0.f, 0.f};
+    if (any_sent) {
+        TreeAcc<LEV, E> tree;
+        uint32_t cnt = 0;
+        for (int32_t g0 = 0; g0 < W; g0 += 64) {
+            const int gi = g0 >> 6;
+            const uint64_t mc = pick(gi, mc0, mc1, mc2, mc3), mp = pick(gi, mp0, mp1, mp2, mp3);
+            const uint64_t mine = pick(gi, p0, p1, p2, p3);
+            const bool vec = gi == 0 ? v0 : gi == 1 ? v1 : gi == 2 ? v2 : v3;
+            const int32_t gn = W - g0 < 64 ? W - g0 : 64;
+            for (int32_t u0 = 0; u0 < gn; u0 += kUnroll) {
+                v4u x[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    x[u] = v4u{0u, 0u, 0u, 0u};
+                    const int32_t b = u0 + u;
+                    if (b < gn && ((mc >> b) & 1ull) && valid) {
+                        if ((mp >> b) & 1ull)
+                            x[u] = load_grad<FP16>(vec, mine, b, byte_off, layer_ptrs, offsets, L, g0 + b, la, ea,
+                                                   i0, P);
+                        else
+                            x[u] = __builtin_nontemporal_load(
+                                reinterpret_cast<const v4u*>(resid + (int64_t)(g0 + b) * ld + i0));
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int32_t b = u0 + u;
+                    if (b < gn) {
+                        const int kind = (((mc & mp) >> b) & 1ull) ? (vec ? kGradVec : kReady) : kResid;
+                        const float4 a = decode_leaf<FP16>(x[u], kind);
+                        float f[E] = {a.x, a.y, a.z, a.w};
+                        tree.push(f, cnt);
+                        ++cnt;
+                    }
+                }
+            }
+        }
+        tree.result((uint32_t)W, s);
+    }
+
+    // Chunks sent in the previous step but not now: their residual is the
+    // widened gradient (plus +0).  Up to 8 workers' loads are in flight
+    // before their stores.
+    if (any_prev && valid) {
+        for (int32_t g0 = 0; g0 < W; g0 += 64) {
+            const int gi = g0 >> 6;
+            uint64_t m = pick(gi, mp0, mp1, mp2, mp3) & ~pick(gi, mc0, mc1, mc2, mc3);
+            const uint64_t mine = pick(gi, p0, p1, p2, p3);
+            const bool vec = gi == 0 ? v0 : gi == 1 ? v1 : gi == 2 ? v2 : v3;
+            while (m != 0ull) {
+                int bs[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    bs[q] = -1;
+                    if (m != 0ull) {
+                        bs[q] = __builtin_ctzll(m);
+                        m &= m - 1ull;
+                    }
+                }
+                v4u x[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (bs[q] >= 0)
+                        x[q] = load_grad<FP16>(vec, mine, bs[q], byte_off, layer_ptrs, offsets, L, g0 + bs[q], la,
+                                               ea, i0, P);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (bs[q] >= 0) {
+                        const float4 a = decode_leaf<FP16>(x[q], vec ? kGradVec : kReady);
+                        float* r = resid + (int64_t)(g0 + bs[q]) * ld + i0;
+                        if (full) {
+                            *reinterpret_cast<float4*>(r) = a;
+                        } else {
+                            const float av[4] = {a.x, a.y, a.z, a.w};
+                            for (int e = 0; e < 4; ++e)
+                                if (i0 + e < P) r[e] = av[e];
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    if (!valid) return;
+    float g[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) g[e] = s[e] * invW;
+    if (full) {
+        if (grad) *reinterpret_cast<float4*>(grad + i0) = make_float4(g[0], g[1], g[2], g[3]);
+        if (do_sgd) {
+            sgd_update(g[0], lr, mu, wv.x, vv.x);
+            sgd_update(g[1], lr, mu, wv.y, vv.y);
+            sgd_update(g[2], lr, mu, wv.z, vv.z);
+            sgd_update(g[3], lr, mu, wv.w, vv.w);
+            *reinterpret_cast<float4*>(w + i0) = wv;
+            *reinterpret_cast<float4*>(v + i0) = vv;
+        }
+    } else {
+        for (int e = 0; e < E; ++e) {
+            if (i0 + e < P) {
+                if (grad) grad[i0 + e] = g[e];
+                if (do_sgd) {
+                    float we = w[i0 + e], ve = v[i0 + e];
+                    sgd_update(g[e], lr, mu, we, ve);
+                    w[i0 + e] = we;
+                    v[i0 + e] = ve;
+                }
+            }
+        }
+    }
+}
+
+template <int LEV>
+hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
+                          const uint32_t* sel_mask, float* grad, const ga_sgd* sgd, float* w, float* v,
+                          hipStream_t s) {
+    const int64_t threads = (p.P + 3) / 4;
+    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const float invW = (float)(1.0 / (double)p.W);
+    const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
+    if (p.dtype == GA_FP16)
+        hipLaunchKernelGGL((k_gather_defer<LEV, true>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets,
+                           p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask, sel_mask, p.mw,
+                           invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    else
+        hipLaunchKernelGGL((k_gather_defer<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask,
+                           sel_mask, p.mw, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
+                                      const uint32_t* prev_mask, const uint32_t* sel_mask, float* grad,
+                                      const ga_sgd* sgd, float* w, float* v, hipStream_t s) {
+    if (p.P == 0) return hipSuccess;
+    if (p.W < (1 << 5)) return defer_dispatch<5>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
+    if (p.W < (1 << 8)) return defer_dispatch<8>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
+    return hipErrorNotSupported;  // W >= 256: rejected by the ABI before launch
+}
+
+}  // namespace ga

@@ -35,7 +35,7 @@ __device__ __forceinline__ double wave_sum(double x) {
 // (src typed by FP16), residual element i is r[i].  With vec_ok, ss is a
 // multiple of 8 and src + (ss - soff) is 16-byte aligned, so the body runs on
 // 8-element vectors; the rest goes element by element.
-template <bool FP16>
+template <bool FP16, bool STORE = true>
 __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_t soff, bool vec_ok,
                                              float* __restrict__ r, int64_t ss, int64_t se, bool rzero,
                                              double& acc0, double& acc1) {
@@ -73,8 +73,10 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
             a0.z = lf[u][2] + r0[u].z; a0.w = lf[u][3] + r0[u].w;
             a1.x = lf[u][4] + r1[u].x; a1.y = lf[u][5] + r1[u].y;
             a1.z = lf[u][6] + r1[u].z; a1.w = lf[u][7] + r1[u].w;
-            *reinterpret_cast<float4*>(r + i) = a0;
-            *reinterpret_cast<float4*>(r + i + 4) = a1;
+            if (STORE) {
+                *reinterpret_cast<float4*>(r + i) = a0;
+                *reinterpret_cast<float4*>(r + i + 4) = a1;
+            }
             acc0 = fma((double)a0.x, (double)a0.x, acc0);
             acc1 = fma((double)a0.y, (double)a0.y, acc1);
             acc0 = fma((double)a0.z, (double)a0.z, acc0);
@@ -98,7 +100,7 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const float a = lf[q] + (rzero ? 0.f : r[i + q]);
-            r[i + q] = a;
+            if (STORE) r[i + q] = a;
             acc0 = fma((double)a, (double)a, acc0);
         }
     }
@@ -106,7 +108,7 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
         const float lf = FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i - soff])
                               : static_cast<gptr<float>>(src)[i - soff];
         const float a = lf + (rzero ? 0.f : r[i]);
-        r[i] = a;
+        if (STORE) r[i] = a;
         acc0 = fma((double)a, (double)a, acc0);
     }
 }
@@ -115,7 +117,11 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
 // the W*L per-layer tensors of the layer table (zero-copy fusion: the chunk's
 // elements are gathered from the layers it overlaps); otherwise from the
 // flat [W][ld] bucket.
-template <bool FP16, bool LAZY, bool LAYERS>
+// DEFER (lazy mode, layer tensors only): a chunk sent in the previous step
+// computes its key but does not store a, which is the widened gradient; the
+// deferred gather reads the gradient for it instead, and writes it as the
+// residual if the chunk is not sent again.
+template <bool FP16, bool LAZY, bool LAYERS, bool DEFER = false>
 __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     const void* __restrict__ bucket, const uint64_t* __restrict__ layer_ptrs,
     const int64_t* __restrict__ offsets, int32_t L, float* __restrict__ resid, int64_t ld, int64_t P,
@@ -142,8 +148,12 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
             const int64_t off = offsets[l], end = offsets[l + 1];
             const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
             const bool vec_ok = (off & 7) == 0 && (addr & 15) == 0;
-            norm_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e,
-                               rzero, acc0, acc1);
+            if (DEFER && rzero)
+                norm_segment<FP16, false>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s,
+                                          end < e ? end : e, rzero, acc0, acc1);
+            else
+                norm_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e,
+                                   rzero, acc0, acc1);
         }
     } else {
         const uint64_t row = reinterpret_cast<uint64_t>(bucket) + (uint64_t)(w * ld * (FP16 ? 2 : 4));
@@ -163,16 +173,17 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     }
 }
 
-template <bool LAYERS>
+template <bool LAYERS, bool DEFER = false>
 hipError_t norm_dispatch(const Plan& p, const void* bucket, const uint64_t* layer_ptrs, float* resid,
                          const uint32_t* prev_mask, double* keys, hipStream_t s) {
     const int64_t blocks = (int64_t)p.W * p.n_c;
     if (blocks == 0) return hipSuccess;
     const bool f16 = p.dtype == GA_FP16;
     const int32_t n_c = (int32_t)p.n_c;
-#define GA_NORM_LAUNCH(F, Z)                                                                                 \
-    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS>), dim3((unsigned)blocks), dim3(kNormThreads), 0, s, bucket, \
-                       layer_ptrs, p.d_offsets, p.L, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys)
+#define GA_NORM_LAUNCH(F, Z)                                                                             \
+    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z>), dim3((unsigned)blocks), dim3(kNormThreads), \
+                       0, s, bucket, layer_ptrs, p.d_offsets, p.L, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, \
+                       keys)
     if (f16 && prev_mask) GA_NORM_LAUNCH(true, true);
     else if (f16) GA_NORM_LAUNCH(true, false);
     else if (prev_mask) GA_NORM_LAUNCH(false, true);
@@ -191,6 +202,11 @@ hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid, co
 hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, float* resid,
                                     const uint32_t* prev_mask, double* keys, hipStream_t s) {
     return norm_dispatch<true>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s);
+}
+
+hipError_t launch_chunk_norm_layers_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
+                                          const uint32_t* prev_mask, double* keys, hipStream_t s) {
+    return norm_dispatch<true, true>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s);
 }
 
 }  // namespace ga

@@ -39,6 +39,16 @@ hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid,
                              const uint32_t* prev_mask, double* keys, hipStream_t s);
 hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, float* resid,
                                     const uint32_t* prev_mask, double* keys, hipStream_t s);
+// launch_chunk_norm_layers in deferred mode (prev_mask required): a chunk
+// sent in the previous step does not store its a.
+hipError_t launch_chunk_norm_layers_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
+                                          const uint32_t* prev_mask, double* keys, hipStream_t s);
+// Gather-reduce for deferred mode: a chunk sent now and in the previous step
+// is read from the gradient tensors; one sent before but not now gets its
+// residual (the widened gradient) written.  C must be a multiple of 256.
+hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
+                                      const uint32_t* prev_mask, const uint32_t* sel_mask, float* grad,
+                                      const ga_sgd* sgd, float* w, float* v, hipStream_t s);
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
 // launch_tree_layers over a sub-list of layers: worker w's layer l is entry

@@ -249,6 +249,45 @@ ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const 
                                   float* d_w, float* d_v, hipStream_t stream);
 
 /*
+ * Coarse-grained sparse communication [GF] in deferred-residual form, for
+ * gradients held as per-layer tensors (a lazy-zero mode that moves fewer
+ * bytes).  A chunk a worker sent in the previous step has a zero residual, so
+ * its a is the worker's widened gradient; the norm pass does not store it and
+ * the gather reads the gradient instead.  One step is
+ *   ga_chunk_norm_layers_defer(prev) -> ga_chunk_topk(cur) ->
+ *   ga_sparse_gather_reduce_layers_defer(prev, cur)
+ * with two mask buffers that swap roles every step (the first step passes an
+ * all-zero prev).  Keys, selection, mean gradient, w and v are those of the
+ * lazy-zero sequence of ga_chunk_norm_layers / ga_sparse_gather_reduce, bit
+ * for bit, and after the gather d_residual holds what that sequence leaves:
+ * the new residual, with the chunks sent now read as zero (pass cur as the
+ * next step's prev).
+ *
+ * ga_chunk_norm_layers_defer: as ga_chunk_norm_layers with d_prev_mask
+ *   required; for a chunk set in d_prev_mask, a is not stored (d_residual keeps
+ *   stale values there).
+ */
+ga_status ga_chunk_norm_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
+                                     const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream);
+
+/*
+ * ga_sparse_gather_reduce_layers_defer: the gather-reduce of the step, with
+ * the step's gradient tensors (d_layer_ptrs, as in ga_chunk_norm_layers):
+ *   leaf of worker w, chunk c sent now (d_sel_mask) = widened gradient + 0
+ *     if c was also sent in the previous step (d_prev_mask), else d_residual;
+ *   a chunk set in d_prev_mask but not in d_sel_mask gets d_residual = the
+ *     widened gradient + 0 (its residual after this step);
+ *   then the tree, mean and SGD of ga_sparse_gather_reduce.
+ * d_prev_mask and d_sel_mask must be different buffers; the chunk size must be
+ * a multiple of 256 elements and W below 256 (GA_ERR_UNSUPPORTED otherwise).  d_grad, sgd,
+ * d_w, d_v: as in ga_tree_reduce.
+ */
+ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
+                                               const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
+                                               float* d_grad, const ga_sgd* sgd, float* d_w, float* d_v,
+                                               hipStream_t stream);
+
+/*
  * Momentum SGD on binary32 master weights, Caffe form (FireCaffe runs Caffe
  * models and reproduces Caffe's numbers [FC FAQ]), per element:
  *   v <- fl(fl(mu * v) + fl(lr * g));   w <- fl(w - v)

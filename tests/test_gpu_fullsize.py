@@ -146,3 +146,51 @@ def test_buckets_alexnet16_full_size(ga, cap):
         assert_same_bits(host(wd), w_ref, "w")
         assert_same_bits(host(vd), v_ref, "v")
         log("alexnet16 buckets (cap %d) step %d ok in %.1fs" % (cap, step, time.time() - t0))
+
+
+def test_sparse_alexnet128_full_size_deferred(ga):
+    """The AlexNet-shaped W=128 sparse workload as benchmarked by default: 2048
+    per-layer tensors, 3 consecutive steps in deferred lazy-zero mode (two
+    mask buffers), every output compared with the oracle."""
+    wl = workloads.WORKLOADS["alexnet128_sparse"]
+    C = wl.chunk
+    plan = ga.Plan(wl.W, wl.numels, True, chunk=C, keep_ratio=wl.rho)
+    P, ld, k, n_c = wl.P, plan.ld, plan.k, plan.n_chunks
+    seg = workloads.segments(wl)
+    w_ref = workloads.weights(wl)
+    v_ref = np.zeros(P, np.float32)
+    r_ref = np.zeros((wl.W, ld), np.float32)
+    wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
+    rd = plan.empty_residual()
+    keys = plan.empty_keys()
+    idx = torch.empty((wl.W, k), dtype=torch.int32, device="cuda")
+    masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(2)]
+    gd = torch.empty(P, dtype=torch.float32, device="cuda")
+    sample = [0, 1, 63, 127]
+    for step in (1, 2, 3):
+        t0 = time.time()
+        b = workloads.grad_bucket(wl, step, ld, seg=seg)
+        buf, ptrs = device_layers(b[:, :P], wl.numels)
+        res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
+        del b
+        prev, cur = masks[(step + 1) % 2], masks[step % 2]
+        plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
+        plan.chunk_topk(keys, idx, cur)
+        plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        torch.cuda.synchronize()
+        del buf
+        assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
+        assert np.array_equal(host(idx), res.sel_idx), "selected chunk indices differ"
+        assert np.array_equal(host(cur).view(np.uint32), res.sel_mask)
+        assert_close(host(keys), res.keys, KEY_RTOL, "keys")
+        assert_same_bits(host(gd), res.gbar, "gbar")
+        assert_same_bits(host(wd), w_ref, "w")
+        assert_same_bits(host(vd), v_ref, "v")
+        m = host(cur).view(np.uint32)
+        for w in sample:
+            r = host(rd[w, :P]).copy()
+            for c in range(n_c):
+                if (int(m[w, c >> 5]) >> (c & 31)) & 1:
+                    r[c * C:min((c + 1) * C, P)] = 0.0
+            assert_same_bits(r, r_ref[w, :P], "residual of worker %d" % w)
+        log("deferred step %d compared in %.1fs" % (step, time.time() - t0))
