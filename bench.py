@@ -305,9 +305,9 @@ def main():
                   "gather_sgd": W * plan.k * plan.chunk * 4 + 16 * P}
     else:
         kbytes = {"tree_sgd": b_alg}
-    for nm, nb in kbytes.items():
-        per_kernel[nm]["bytes_alg"] = nb
-        per_kernel[nm]["GBps_alg"] = round(nb / (per_kernel[nm]["mean_ms"] * 1e-3) / 1e9, 1)
+    for nm, kb in kbytes.items():
+        per_kernel[nm]["bytes_alg"] = kb
+        per_kernel[nm]["GBps_alg"] = round(kb / (per_kernel[nm]["mean_ms"] * 1e-3) / 1e9, 1)
         per_kernel[nm]["frac_hbm_peak"] = round(per_kernel[nm]["GBps_alg"] / HBM_PEAK_GBPS, 4)
     dom_ms = per_kernel[dom]["mean_ms"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
