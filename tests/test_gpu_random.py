@@ -3,7 +3,8 @@ path that applies to it and compared with the oracle element by element:
 random worker counts, layer lists (aligned and ragged sizes, small and large
 layers), binary16 or binary32 gradients, chunk sizes and keep ratios, both
 residual modes, zero-copy tensors at random misalignments, and multi-bucket
-schedules at random thresholds.  The case is printed before it runs."""
+schedules at random thresholds, the deferred residual form where it applies.
+The case is printed before it runs."""
 import numpy as np
 import pytest
 
@@ -40,12 +41,15 @@ def draw(seed):
         numels.append(n)
     fp16 = bool(rng.random() < 0.6)
     sparse = bool(rng.random() < 0.5)
-    chunk = 8 * int(rng.integers(1, 65)) if sparse else 0
+    chunk = (256 * int(rng.integers(1, 4)) if rng.random() < 0.4 else 8 * int(rng.integers(1, 65))) if sparse else 0
     rho = float(rng.choice([0.0, 0.05, 0.1, 0.25, 0.5, 1.0, rng.random()])) if sparse else 0.0
     lazy = bool(rng.random() < 0.5)
+    # deferred residual where it applies (C a multiple of 256, W < 256)
+    deferred = bool(sparse and chunk % 256 == 0 and W < 256 and rng.random() < 0.7)
     mis = int(rng.integers(0, 4))
     thr = int(rng.choice([1, 64, 1024, 16384, 1 << 30]))
-    return dict(W=W, numels=numels, fp16=fp16, sparse=sparse, chunk=chunk, rho=rho, lazy=lazy, mis=mis, thr=thr)
+    return dict(W=W, numels=numels, fp16=fp16, sparse=sparse, chunk=chunk, rho=rho, lazy=lazy or deferred,
+                deferred=deferred, mis=mis, thr=thr)
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
@@ -95,9 +99,14 @@ def test_random_case(ga, seed):
         res = oracle.sparse_step(b, P, fp16, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         cur, prev = masks[step % 2], masks[(step + 1) % 2]
         buf, ptrs = device_layers(b[:, :P], numels, misalign)
-        plan.chunk_norm_layers(ptrs, rd, keys, prev if (c["lazy"] and step > 1) else None)
-        plan.chunk_topk(keys, idx, cur)
-        plan.sparse_gather_reduce(rd, cur, not c["lazy"], gd, wd, vd, wl.lr, wl.mu)
+        if c["deferred"]:
+            plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        else:
+            plan.chunk_norm_layers(ptrs, rd, keys, prev if (c["lazy"] and step > 1) else None)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce(rd, cur, not c["lazy"], gd, wd, vd, wl.lr, wl.mu)
         torch.cuda.synchronize()
         if not np.all(res.margin > 1e-12):
             pytest.skip("selection boundary too close to certify at seed %d" % seed)
