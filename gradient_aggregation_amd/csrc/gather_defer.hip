@@ -7,13 +7,14 @@
 // pass does not store that a.  This gather then
 //   - takes the leaf of a chunk sent now and in the previous step from the
 //     gradient tensors (2 bytes per binary16 element instead of 4),
-//   - writes the residual of a chunk sent in the previous step but not now
-//     (the widened gradient), so that afterwards the residual buffer holds
-//     exactly what the non-deferred lazy mode leaves,
 //   - and otherwise reduces like k_gather_wave: every worker pushes its leaf or
-//     +0 into the fixed tree, then the mean and the fused SGD update.
-// A wavefront covers 256 consecutive elements of one chunk (C is a multiple of
-// 256), so the two mask bits of a worker are wavefront-uniform.
+//     +0 into the fixed tree, then the mean and the fused SGD update
+//     (k_gather_defer; a wavefront covers 256 consecutive elements of one
+//     chunk, C being a multiple of 256, so a worker's two mask bits are
+//     wavefront-uniform);
+//   - and writes the residual of a chunk sent in the previous step but not now
+//     (the widened gradient), so that afterwards the residual buffer holds
+//     exactly what the non-deferred lazy mode leaves (k_materialize).
 #include "device.h"
 #include "plan.h"
 #include "tree.h"
@@ -134,7 +135,9 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     const uint64_t mp0 = __ballot((pw[0] & cb) != 0u), mp1 = __ballot((pw[1] & cb) != 0u);
     const uint64_t mp2 = __ballot((pw[2] & cb) != 0u), mp3 = __ballot((pw[3] & cb) != 0u);
     const bool any_sent = (mc0 | mc1 | mc2 | mc3) != 0ull;
-    const bool any_prev = (mp0 | mp1 | mp2 | mp3) != 0ull;
+    // some worker sent the chunk now and in the previous step: its leaf is
+    // read from the gradient tensor
+    const bool any_resent = ((mc0 & mp0) | (mc1 & mp1) | (mc2 & mp2) | (mc3 & mp3)) != 0ull;
 
     float4 wv = make_float4(0.f, 0.f, 0.f, 0.f), vv = wv;
     if (do_sgd && full) {
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     // tiles), and vN says every address of group N allows the vector load
     uint64_t p0 = 0ull, p1 = 0ull, p2 = 0ull, p3 = 0ull;
     bool v0 = false, v1 = false, v2 = false, v3 = false;
-    if (any_prev) {
+    if (any_resent) {
         const uint32_t tinfo = tile_layer[wave_base / tile_elems];
         l0 = (int32_t)(tinfo & 0x7fffffffu);
         off0 = offsets[l0];
@@ -224,49 +227,6 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
         tree.result((uint32_t)W, s);
     }
 
-    // Chunks sent in the previous step but not now: their residual is the
-    // widened gradient (plus +0).  Up to 8 workers' loads are in flight
-    // before their stores.
-    if (any_prev && valid) {
-        for (int32_t g0 = 0; g0 < W; g0 += 64) {
-            const int gi = g0 >> 6;
-            uint64_t m = pick(gi, mp0, mp1, mp2, mp3) & ~pick(gi, mc0, mc1, mc2, mc3);
-            const uint64_t mine = pick(gi, p0, p1, p2, p3);
-            const bool vec = gi == 0 ? v0 : gi == 1 ? v1 : gi == 2 ? v2 : v3;
-            while (m != 0ull) {
-                int bs[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    bs[q] = -1;
-                    if (m != 0ull) {
-                        bs[q] = __builtin_ctzll(m);
-                        m &= m - 1ull;
-                    }
-                }
-                v4u x[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (bs[q] >= 0)
-                        x[q] = load_grad<FP16>(vec, mine, bs[q], byte_off, layer_ptrs, offsets, L, g0 + bs[q], la,
-                                               ea, i0, P);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (bs[q] >= 0) {
-                        const float4 a = decode_leaf<FP16>(x[q], vec ? kGradVec : kReady);
-                        float* r = resid + (int64_t)(g0 + bs[q]) * ld + i0;
-                        if (full) {
-                            *reinterpret_cast<float4*>(r) = a;
-                        } else {
-                            const float av[4] = {a.x, a.y, a.z, a.w};
-                            for (int e = 0; e < 4; ++e)
-                                if (i0 + e < P) r[e] = av[e];
-                        }
-                    }
-                }
-            }
-        }
-    }
-
     if (!valid) return;
     float g[E];
 #pragma unroll
@@ -296,6 +256,87 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     }
 }
 
+// Residual = widened gradient (plus +0) on the elements [ss, se) of one
+// worker, whose gradient element i is src[i - soff]; with vec_ok, ss is a
+// multiple of 8 and src + (ss - soff) is 16-byte aligned.
+template <bool FP16>
+__device__ __forceinline__ void copy_segment(gptr<void> __restrict__ src, int64_t soff, bool vec_ok,
+                                             float* __restrict__ r, int64_t ss, int64_t se) {
+    constexpr int UN = 4;
+    const int64_t nvec = vec_ok ? (se - ss) >> 3 : 0;
+    int64_t j = threadIdx.x;
+    for (; j + (UN - 1) * kThreads < nvec; j += UN * kThreads) {
+        float f[UN][8];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int64_t i = ss + ((j + u * kThreads) << 3);
+            if (FP16) {
+                widen8(load_u4(static_cast<gptr<uint16_t>>(src) + (i - soff)), f[u]);
+            } else {
+                gptr<float> gp = static_cast<gptr<float>>(src) + (i - soff);
+                const float4 g0 = load_f4(gp), g1 = load_f4(gp + 4);
+                f[u][0] = g0.x; f[u][1] = g0.y; f[u][2] = g0.z; f[u][3] = g0.w;
+                f[u][4] = g1.x; f[u][5] = g1.y; f[u][6] = g1.z; f[u][7] = g1.w;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int64_t i = ss + ((j + u * kThreads) << 3);
+            *reinterpret_cast<float4*>(r + i) =
+                make_float4(f[u][0] + 0.f, f[u][1] + 0.f, f[u][2] + 0.f, f[u][3] + 0.f);
+            *reinterpret_cast<float4*>(r + i + 4) =
+                make_float4(f[u][4] + 0.f, f[u][5] + 0.f, f[u][6] + 0.f, f[u][7] + 0.f);
+        }
+    }
+    for (; j < nvec; j += kThreads) {
+        const int64_t i = ss + (j << 3);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            r[i + q] = (FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i + q - soff])
+                             : static_cast<gptr<float>>(src)[i + q - soff]) + 0.f;
+    }
+    for (int64_t i = ss + (nvec << 3) + threadIdx.x; i < se; i += kThreads)
+        r[i] = (FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i - soff]) : static_cast<gptr<float>>(src)[i - soff]) +
+               0.f;
+}
+
+// One workgroup per (worker, 32-chunk mask word): it writes the chunks of that
+// word the worker sent in the previous step but not now (their residual is
+// the widened gradient), one after the other.  Most words have none or one,
+// so the grid stays small instead of a workgroup per (worker, chunk).
+template <bool FP16>
+__global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __restrict__ layer_ptrs,
+                                                          const int64_t* __restrict__ offsets, int32_t L,
+                                                          float* __restrict__ resid, int64_t ld, int64_t P, int64_t C,
+                                                          int32_t n_c, const uint32_t* __restrict__ prev_mask,
+                                                          const uint32_t* __restrict__ sel_mask, int32_t mw) {
+    const int64_t b = blockIdx.x;
+    const int32_t w = (int32_t)(b / mw);
+    const int32_t q = (int32_t)(b - (int64_t)w * mw);
+    const int64_t word = (int64_t)w * mw + q;
+    uint32_t bits = prev_mask[word] & ~sel_mask[word];
+    float* __restrict__ r = resid + (int64_t)w * ld;
+    while (bits != 0u) {
+        const int32_t c = q * 32 + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        if (c >= n_c) break;
+        const int64_t s = (int64_t)c * C;
+        const int64_t e = s + C < P ? s + C : P;
+        int32_t lo = 0, hi = L;   // first layer ending after s
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) >> 1;
+            if (offsets[mid + 1] <= s) lo = mid + 1;
+            else hi = mid;
+        }
+        for (int32_t l = lo; l < L && offsets[l] < e; ++l) {
+            const int64_t off = offsets[l], end = offsets[l + 1];
+            const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
+            const bool vec_ok = (off & 7) == 0 && (addr & 15) == 0;
+            copy_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e);
+        }
+    }
+}
+
 template <int LEV>
 hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
                           const uint32_t* sel_mask, float* grad, const ga_sgd* sgd, float* w, float* v,
@@ -312,6 +353,17 @@ hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resi
         hipLaunchKernelGGL((k_gather_defer<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs,
                            p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask,
                            sel_mask, p.mw, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the (worker, chunk) pairs written here are disjoint from those the
+    // reduction reads, so the order of the two launches does not matter
+    const int64_t words = (int64_t)p.W * p.mw;
+    if (p.dtype == GA_FP16)
+        hipLaunchKernelGGL((k_materialize<true>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c, prev_mask, sel_mask, p.mw);
+    else
+        hipLaunchKernelGGL((k_materialize<false>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c, prev_mask, sel_mask, p.mw);
     return hipGetLastError();
 }
 
