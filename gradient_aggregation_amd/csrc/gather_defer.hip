@@ -300,28 +300,36 @@ __device__ __forceinline__ void copy_segment(gptr<void> __restrict__ src, int64_
                0.f;
 }
 
-// One workgroup per (worker, 32-chunk mask word): it writes the chunks of that
-// word the worker sent in the previous step but not now (their residual is
-// the widened gradient), one after the other.  Most words have none or one,
-// so the grid stays small instead of a workgroup per (worker, chunk).
+// kMatParts workgroups per (worker, 32-chunk mask word): they write, each its
+// share of every chunk, the chunks of that word the worker sent in the
+// previous step but not now (their residual is the widened gradient).  Most
+// words have none or one such chunk, so the grid stays far smaller than one
+// workgroup per (worker, chunk).
+constexpr int kMatParts = 4;
 template <bool FP16>
 __global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __restrict__ layer_ptrs,
                                                           const int64_t* __restrict__ offsets, int32_t L,
                                                           float* __restrict__ resid, int64_t ld, int64_t P, int64_t C,
                                                           int32_t n_c, const uint32_t* __restrict__ prev_mask,
                                                           const uint32_t* __restrict__ sel_mask, int32_t mw) {
-    const int64_t b = blockIdx.x;
+    const int64_t b = blockIdx.x / kMatParts;
+    const int32_t part = (int32_t)(blockIdx.x % kMatParts);
     const int32_t w = (int32_t)(b / mw);
     const int32_t q = (int32_t)(b - (int64_t)w * mw);
     const int64_t word = (int64_t)w * mw + q;
     uint32_t bits = prev_mask[word] & ~sel_mask[word];
     float* __restrict__ r = resid + (int64_t)w * ld;
+    // this workgroup's share of each chunk: a multiple of 8 elements
+    const int64_t share = (C / kMatParts + 7) / 8 * 8;
     while (bits != 0u) {
         const int32_t c = q * 32 + __builtin_ctz(bits);
         bits &= bits - 1u;
         if (c >= n_c) break;
-        const int64_t s = (int64_t)c * C;
-        const int64_t e = s + C < P ? s + C : P;
+        const int64_t c0 = (int64_t)c * C;
+        const int64_t c1 = c0 + C < P ? c0 + C : P;
+        const int64_t s = c0 + part * share < c1 ? c0 + part * share : c1;
+        const int64_t e = s + share < c1 ? s + share : c1;
+        if (s >= e) continue;
         int32_t lo = 0, hi = L;   // first layer ending after s
         while (lo < hi) {
             const int32_t mid = (lo + hi) >> 1;
@@ -357,7 +365,7 @@ hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resi
     if (e != hipSuccess) return e;
     // the (worker, chunk) pairs written here are disjoint from those the
     // reduction reads, so the order of the two launches does not matter
-    const int64_t words = (int64_t)p.W * p.mw;
+    const int64_t words = (int64_t)p.W * p.mw * kMatParts;
     if (p.dtype == GA_FP16)
         hipLaunchKernelGGL((k_materialize<true>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
                            p.d_offsets, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c, prev_mask, sel_mask, p.mw);
