@@ -308,7 +308,9 @@ __device__ __forceinline__ void copy_segment(gptr<void> __restrict__ src, int64_
 constexpr int kMatParts = 4;
 template <bool FP16>
 __global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __restrict__ layer_ptrs,
-                                                          const int64_t* __restrict__ offsets, int32_t L,
+                                                          const int64_t* __restrict__ offsets,
+                                                          const uint32_t* __restrict__ tile_layer, int64_t tile_elems,
+                                                          int32_t L,
                                                           float* __restrict__ resid, int64_t ld, int64_t P, int64_t C,
                                                           int32_t n_c, const uint32_t* __restrict__ prev_mask,
                                                           const uint32_t* __restrict__ sel_mask, int32_t mw) {
@@ -330,12 +332,10 @@ __global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __rest
         const int64_t s = c0 + part * share < c1 ? c0 + part * share : c1;
         const int64_t e = s + share < c1 ? s + share : c1;
         if (s >= e) continue;
-        int32_t lo = 0, hi = L;   // first layer ending after s
-        while (lo < hi) {
-            const int32_t mid = (lo + hi) >> 1;
-            if (offsets[mid + 1] <= s) lo = mid + 1;
-            else hi = mid;
-        }
+        // the layer of s: the tile table gives the layer of its tile's first
+        // element, and s lies in that layer or a later one
+        int32_t lo = (int32_t)(tile_layer[s / tile_elems] & 0x7fffffffu);
+        while (offsets[lo + 1] <= s) ++lo;
         for (int32_t l = lo; l < L && offsets[l] < e; ++l) {
             const int64_t off = offsets[l], end = offsets[l + 1];
             const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
@@ -368,10 +368,12 @@ hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resi
     const int64_t words = (int64_t)p.W * p.mw * kMatParts;
     if (p.dtype == GA_FP16)
         hipLaunchKernelGGL((k_materialize<true>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c, prev_mask, sel_mask, p.mw);
+                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
+                           prev_mask, sel_mask, p.mw);
     else
         hipLaunchKernelGGL((k_materialize<false>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c, prev_mask, sel_mask, p.mw);
+                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
+                           prev_mask, sel_mask, p.mw);
     return hipGetLastError();
 }
 
