@@ -121,6 +121,15 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     const int32_t cw = c >> 5;
     const uint32_t cb = 1u << (c & 31);
 
+    // The layer of the wavefront's tile, its start and end (scalar loads, in
+    // flight with the mask words below): the plan's tile table gives the
+    // layer and whether the tile lies in it at an aligned offset (whole).
+    const uint32_t tinfo = tile_layer[wave_base / tile_elems];
+    const int32_t l0 = (int32_t)(tinfo & 0x7fffffffu);
+    const bool whole = (tinfo >> 31) != 0u;
+    const int64_t off0 = offsets[l0];
+    const int64_t end0 = offsets[l0 + 1];
+
     // Both bitmaps of the (at most four) 64-worker groups, every mask word in
     // flight together: sent now (mc), sent in the previous step (mp).
     uint32_t sw[4], pw[4];
@@ -145,21 +154,15 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
         vv = *reinterpret_cast<const float4*>(v + i0);
     }
 
-    // Where the gradient elements live: the plan's tile table gives the layer
-    // of the wavefront's tile and whether the tile lies in it at an aligned
-    // offset (whole); otherwise each lane finds its layer.
-    bool whole = false;
-    int32_t l0 = 0, la = 0;
-    int64_t off0 = 0, ea = 0;
-    // lane l holds worker (64 gi + l)'s tensor address for layer l0 (whole
-    // tiles), and vN says every address of group N allows the vector load
+    // Where the gradient elements live: for a whole tile, lane l holds worker
+    // (64 gi + l)'s tensor address for layer l0 and vN says every address of
+    // group N allows the vector load; otherwise each lane finds its layer
+    // (la, ending at ea).
+    int32_t la = l0;
+    int64_t ea = end0;
     uint64_t p0 = 0ull, p1 = 0ull, p2 = 0ull, p3 = 0ull;
     bool v0 = false, v1 = false, v2 = false, v3 = false;
     if (any_resent) {
-        const uint32_t tinfo = tile_layer[wave_base / tile_elems];
-        l0 = (int32_t)(tinfo & 0x7fffffffu);
-        off0 = offsets[l0];
-        whole = (tinfo >> 31) != 0u;
         if (whole) {
             p0 = lane < W ? layer_ptrs[(int64_t)lane * L + l0] : 0ull;
             p1 = 64 + lane < W ? layer_ptrs[(int64_t)(64 + lane) * L + l0] : 0ull;
@@ -178,10 +181,6 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
             }
             la = lo;
             ea = offsets[lo + 1];
-        }
-        if (whole) {
-            la = l0;
-            ea = offsets[l0 + 1];
         }
     }
     const int64_t byte_off = (i0 - off0) * kEsz;
