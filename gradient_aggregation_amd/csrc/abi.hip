@@ -297,7 +297,6 @@ ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64
     const ga::Plan* p = as_plan(plan);
     if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
     if (p->C % 256 != 0) return fail(GA_ERR_UNSUPPORTED, "chunk=%lld is not a multiple of 256", (long long)p->C);
-    if (p->W >= 256) return fail(GA_ERR_UNSUPPORTED, "W=%d: the deferred gather takes fewer than 256 workers", p->W);
     if (d_prev_mask == d_sel_mask) return fail(GA_ERR_INVALID, "previous and current masks are the same buffer");
     if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
     if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");

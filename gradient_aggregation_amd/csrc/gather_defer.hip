@@ -99,6 +99,19 @@ __device__ __forceinline__ uint64_t pick(int gi, uint64_t a0, uint64_t a1, uint6
     return gi == 0 ? a0 : gi == 1 ? a1 : gi == 2 ? a2 : a3;
 }
 
+// The bitmaps of the 64-worker group starting at g0 for chunk bit cb of mask
+// word cw: sent now (mc) and sent in the previous step (mp).
+__device__ __forceinline__ void group_masks(const uint32_t* __restrict__ sel_mask,
+                                            const uint32_t* __restrict__ prev_mask, int32_t W, int32_t mw,
+                                            int32_t cw, uint32_t cb, int32_t g0, int lane, uint64_t& mc,
+                                            uint64_t& mp) {
+    const int32_t wk = g0 + lane;
+    const uint32_t sc = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
+    const uint32_t sp = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
+    mc = __ballot((sc & cb) != 0u);
+    mp = __ballot((sp & cb) != 0u);
+}
+
 template <int LEV, bool FP16>
 __global__ __launch_bounds__(kThreads) void k_gather_defer(
     const uint64_t* __restrict__ layer_ptrs, const int64_t* __restrict__ offsets,
@@ -106,7 +119,9 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     int64_t ld, int32_t W, int64_t P, int64_t C, const uint32_t* __restrict__ prev_mask,
     const uint32_t* __restrict__ sel_mask, int32_t mw, float invW, float* __restrict__ grad, int32_t do_sgd,
     float lr, float mu, float* __restrict__ w, float* __restrict__ v) {
-    static_assert(LEV <= 8, "the deferred gather keeps at most four 64-worker groups in registers");
+    // W < 256 (LEV <= 8): the (at most four) groups' bitmaps and addresses
+    // are read once and kept in registers; otherwise group by group.
+    constexpr bool kCached = LEV <= 8;
     constexpr int E = 4;
     constexpr int64_t kEsz = FP16 ? 2 : 4;
     constexpr uint64_t kAlignMask = FP16 ? 7ull : 15ull;
@@ -132,21 +147,36 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
 
     // Both bitmaps of the (at most four) 64-worker groups, every mask word in
     // flight together: sent now (mc), sent in the previous step (mp).
-    uint32_t sw[4], pw[4];
+    uint64_t mc0 = 0ull, mc1 = 0ull, mc2 = 0ull, mc3 = 0ull, mp0 = 0ull, mp1 = 0ull, mp2 = 0ull, mp3 = 0ull;
+    bool any_sent = false, any_resent = false;
+    if (kCached) {
+        uint32_t sw[4], pw[4];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-        const int32_t wk = gi * 64 + lane;
-        sw[gi] = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
-        pw[gi] = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
+        for (int gi = 0; gi < 4; ++gi) {
+            const int32_t wk = gi * 64 + lane;
+            sw[gi] = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
+            pw[gi] = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
+        }
+        mc0 = __ballot((sw[0] & cb) != 0u);
+        mc1 = __ballot((sw[1] & cb) != 0u);
+        mc2 = __ballot((sw[2] & cb) != 0u);
+        mc3 = __ballot((sw[3] & cb) != 0u);
+        mp0 = __ballot((pw[0] & cb) != 0u);
+        mp1 = __ballot((pw[1] & cb) != 0u);
+        mp2 = __ballot((pw[2] & cb) != 0u);
+        mp3 = __ballot((pw[3] & cb) != 0u);
+        any_sent = (mc0 | mc1 | mc2 | mc3) != 0ull;
+        // some worker sent the chunk now and in the previous step: its leaf is
+        // read from the gradient tensor
+        any_resent = ((mc0 & mp0) | (mc1 & mp1) | (mc2 & mp2) | (mc3 & mp3)) != 0ull;
+    } else {
+        for (int32_t g0 = 0; g0 < W; g0 += 64) {
+            uint64_t mc, mp;
+            group_masks(sel_mask, prev_mask, W, mw, cw, cb, g0, lane, mc, mp);
+            any_sent |= mc != 0ull;
+            any_resent |= (mc & mp) != 0ull;
+        }
     }
-    const uint64_t mc0 = __ballot((sw[0] & cb) != 0u), mc1 = __ballot((sw[1] & cb) != 0u);
-    const uint64_t mc2 = __ballot((sw[2] & cb) != 0u), mc3 = __ballot((sw[3] & cb) != 0u);
-    const uint64_t mp0 = __ballot((pw[0] & cb) != 0u), mp1 = __ballot((pw[1] & cb) != 0u);
-    const uint64_t mp2 = __ballot((pw[2] & cb) != 0u), mp3 = __ballot((pw[3] & cb) != 0u);
-    const bool any_sent = (mc0 | mc1 | mc2 | mc3) != 0ull;
-    // some worker sent the chunk now and in the previous step: its leaf is
-    // read from the gradient tensor
-    const bool any_resent = ((mc0 & mp0) | (mc1 & mp1) | (mc2 & mp2) | (mc3 & mp3)) != 0ull;
 
     float4 wv = make_float4(0.f, 0.f, 0.f, 0.f), vv = wv;
     if (do_sgd && full) {
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     uint64_t p0 = 0ull, p1 = 0ull, p2 = 0ull, p3 = 0ull;
     bool v0 = false, v1 = false, v2 = false, v3 = false;
     if (any_resent) {
-        if (whole) {
+        if (whole && kCached) {
             p0 = lane < W ? layer_ptrs[(int64_t)lane * L + l0] : 0ull;
             p1 = 64 + lane < W ? layer_ptrs[(int64_t)(64 + lane) * L + l0] : 0ull;
             p2 = 128 + lane < W ? layer_ptrs[(int64_t)(128 + lane) * L + l0] : 0ull;
@@ -172,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
             v1 = __ballot((p1 & kAlignMask) != 0ull) == 0ull;
             v2 = __ballot((p2 & kAlignMask) != 0ull) == 0ull;
             v3 = __ballot((p3 & kAlignMask) != 0ull) == 0ull;
-        } else if (valid) {
+        } else if (!whole && valid) {
             int32_t lo = l0, hi = L;   // the lane's layer is l0 or a later one
             while (lo < hi) {
                 const int32_t mid = (lo + hi) >> 1;
@@ -191,9 +221,22 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
         uint32_t cnt = 0;
         for (int32_t g0 = 0; g0 < W; g0 += 64) {
             const int gi = g0 >> 6;
-            const uint64_t mc = pick(gi, mc0, mc1, mc2, mc3), mp = pick(gi, mp0, mp1, mp2, mp3);
-            const uint64_t mine = pick(gi, p0, p1, p2, p3);
-            const bool vec = gi == 0 ? v0 : gi == 1 ? v1 : gi == 2 ? v2 : v3;
+            uint64_t mc, mp, mine;
+            bool vec;
+            if (kCached) {
+                mc = pick(gi, mc0, mc1, mc2, mc3);
+                mp = pick(gi, mp0, mp1, mp2, mp3);
+                mine = pick(gi, p0, p1, p2, p3);
+                vec = gi == 0 ? v0 : gi == 1 ? v1 : gi == 2 ? v2 : v3;
+            } else {
+                group_masks(sel_mask, prev_mask, W, mw, cw, cb, g0, lane, mc, mp);
+                mine = 0ull;
+                vec = false;
+                if (whole && (mc & mp) != 0ull) {
+                    mine = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
+                    vec = __ballot((mine & kAlignMask) != 0ull) == 0ull;
+                }
+            }
             const int32_t gn = W - g0 < 64 ? W - g0 : 64;
             for (int32_t u0 = 0; u0 < gn; u0 += kUnroll) {
                 v4u x[kUnroll];
@@ -384,7 +427,7 @@ hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs,
     if (p.P == 0) return hipSuccess;
     if (p.W < (1 << 5)) return defer_dispatch<5>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
     if (p.W < (1 << 8)) return defer_dispatch<8>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
-    return hipErrorNotSupported;  // W >= 256: rejected by the ABI before launch
+    return defer_dispatch<11>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
 }
 
 }  // namespace ga

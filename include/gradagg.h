@@ -279,7 +279,7 @@ ga_status ga_chunk_norm_layers_defer(const ga_plan* plan, const uint64_t* d_laye
  *     widened gradient + 0 (its residual after this step);
  *   then the tree, mean and SGD of ga_sparse_gather_reduce.
  * d_prev_mask and d_sel_mask must be different buffers; the chunk size must be
- * a multiple of 256 elements and W below 256 (GA_ERR_UNSUPPORTED otherwise).  d_grad, sgd,
+ * a multiple of 256 elements (GA_ERR_UNSUPPORTED otherwise).  d_grad, sgd,
  * d_w, d_v: as in ga_tree_reduce.
  */
 ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,

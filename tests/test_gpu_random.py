@@ -44,8 +44,8 @@ def draw(seed):
     chunk = (256 * int(rng.integers(1, 4)) if rng.random() < 0.4 else 8 * int(rng.integers(1, 65))) if sparse else 0
     rho = float(rng.choice([0.0, 0.05, 0.1, 0.25, 0.5, 1.0, rng.random()])) if sparse else 0.0
     lazy = bool(rng.random() < 0.5)
-    # deferred residual where it applies (C a multiple of 256, W < 256)
-    deferred = bool(sparse and chunk % 256 == 0 and W < 256 and rng.random() < 0.7)
+    # deferred residual where it applies (C a multiple of 256)
+    deferred = bool(sparse and chunk % 256 == 0 and rng.random() < 0.7)
     mis = int(rng.integers(0, 4))
     thr = int(rng.choice([1, 64, 1024, 16384, 1 << 30]))
     return dict(W=W, numels=numels, fp16=fp16, sparse=sparse, chunk=chunk, rho=rho, lazy=lazy or deferred,
