@@ -288,9 +288,11 @@ def main():
         args.steps, ms_step, gpu_ms_step,
         ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
 
+    b_in = 2 if wl.fp16 else 4
+    deferred_last = deferred_bytes(plan, masks[(n_steps - 1) % 2], masks[n_steps % 2], P, b_in) if defer else None
+
     pack = time_pack(plan, wl, sources[-1], keep[-1] if layers_src else None, stream)
 
-    b_in = 2 if wl.fp16 else 4
     if sparse:
         b_alg = W * P * (b_in + 4 + 4) + 16 * P
         dom, dom_bytes = "chunk_norm", W * P * (b_in + 4 + 4)
@@ -352,6 +354,7 @@ def main():
         "grad_input_GBps": round(W * P * b_in / (ms_step * 1e-3) / 1e9, 2),
         "kernels": per_kernel,
         "first_step_ms": first_step if sparse else None,
+        "deferred_last_step": deferred_last,
         "roofline": {
             "kernel": dom_kernel,
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -586,6 +589,31 @@ def time_pack(plan, wl, src, layer_tensors, stream):
     return {"kernel": "k_pack", "layers": len(wl.numels), "tensors": wl.W * len(wl.numels),
             "mean_ms": round(float(np.mean(d)), 4), "GBps": round(moved / (np.mean(d) * 1e-3) / 1e9, 1),
             "bytes": moved, "matches_source": ok}
+
+
+def deferred_bytes(plan, prev, cur, P, b_in):
+    """Chunk counts of one deferred step from its two selection masks, and the
+    bytes its gather and materialization move: a chunk sent again is read from
+    the gradient (b_in per element), a newly sent one from the residual (4),
+    and a chunk sent before but not now is copied into the residual (b_in + 4);
+    the gather also reads and writes w and v (16 per element)."""
+    import torch
+    n_c, C = plan.n_chunks, plan.chunk
+    sh = torch.arange(32, device=prev.device, dtype=torch.int32)
+
+    def bits(m):
+        return (((m.unsqueeze(-1) >> sh) & 1) != 0).reshape(m.shape[0], -1)[:, :n_c]
+
+    bp, bc = bits(prev), bits(cur)
+    lens = torch.full((n_c,), C, dtype=torch.float64, device=prev.device)
+    lens[-1] = P - (n_c - 1) * C
+    counts = {nm: int(m.sum()) for nm, m in (("resent", bp & bc), ("new", bc & ~bp), ("materialized", bp & ~bc))}
+    elems = {nm: float((m.double() * lens).sum()) for nm, m in (("resent", bp & bc), ("new", bc & ~bp),
+                                                                 ("materialized", bp & ~bc))}
+    return {"chunks_resent": counts["resent"], "chunks_new": counts["new"],
+            "chunks_materialized": counts["materialized"],
+            "gather_bytes": int(elems["resent"] * b_in + elems["new"] * 4 + 16 * P),
+            "materialize_bytes": int(elems["materialized"] * (b_in + 4))}
 
 
 def measured_traffic(path, kernel):

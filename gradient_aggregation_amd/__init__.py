@@ -24,6 +24,7 @@ GA_FP32, GA_FP16 = 0, 1
 ORDERS = {"tree": 0, "server": 1, "ring": 2}
 MAX_WORKERS = 1024
 MAX_CHUNKS = 65536
+MAX_ELEMENTS = 1 << 33
 
 
 class GAError(RuntimeError):

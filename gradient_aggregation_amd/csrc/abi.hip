@@ -51,8 +51,8 @@ ga_status compute(int32_t W, int32_t L, const int64_t* numel, ga_dtype dt, int64
             return fail(GA_ERR_UNSUPPORTED, "layer sizes too large");
         P += numel[l];
     }
-    // Per-row element indices and rows stay below 2^31 vectors for the grids.
-    if (P > ((int64_t)1 << 35)) return fail(GA_ERR_UNSUPPORTED, "P=%lld too large", (long long)P);
+    if (P > GA_MAX_ELEMENTS)
+        return fail(GA_ERR_UNSUPPORTED, "P=%lld exceeds %lld elements", (long long)P, (long long)GA_MAX_ELEMENTS);
     memset(info, 0, sizeof *info);
     info->P = P;
     info->ld = (P + 63) / 64 * 64;
@@ -385,6 +385,8 @@ ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const 
 ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, float* d_v, const ga_sgd* sgd,
                                 hipStream_t stream) {
     if (P < 0 || !sgd) return fail(GA_ERR_INVALID, "bad size or NULL sgd");
+    if (P > GA_MAX_ELEMENTS)
+        return fail(GA_ERR_UNSUPPORTED, "P=%lld exceeds %lld elements", (long long)P, (long long)GA_MAX_ELEMENTS);
     if (P == 0) return ok();
     if (!d_grad || !d_w || !d_v) return fail(GA_ERR_INVALID, "NULL argument");
     if (!aligned16(d_grad) || !aligned16(d_w) || !aligned16(d_v))

@@ -113,7 +113,7 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
     }
 }
 
-// One workgroup per (worker w, chunk c).  LAYERS: the gradient is read from
+// One workgroup per (worker w = blockIdx.y, chunk c = blockIdx.x).  LAYERS: the gradient is read from
 // the W*L per-layer tensors of the layer table (zero-copy fusion: the chunk's
 // elements are gathered from the layers it overlaps); otherwise from the
 // flat [W][ld] bucket.
@@ -126,9 +126,9 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     const void* __restrict__ bucket, const uint64_t* __restrict__ layer_ptrs,
     const int64_t* __restrict__ offsets, int32_t L, float* __restrict__ resid, int64_t ld, int64_t P,
     int64_t C, int32_t n_c, const uint32_t* __restrict__ prev_mask, int32_t mw, double* __restrict__ keys) {
-    const int64_t b = blockIdx.x;
-    const int32_t w = (int32_t)(b / n_c);
-    const int32_t c = (int32_t)(b - (int64_t)w * n_c);
+    const int32_t w = (int32_t)blockIdx.y;
+    const int32_t c = (int32_t)blockIdx.x;
+    const int64_t b = (int64_t)w * n_c + c;
     const int64_t s = (int64_t)c * C;
     const int64_t e = s + C < P ? s + C : P;
     bool rzero = false;
@@ -176,14 +176,15 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
 template <bool LAYERS, bool DEFER = false>
 hipError_t norm_dispatch(const Plan& p, const void* bucket, const uint64_t* layer_ptrs, float* resid,
                          const uint32_t* prev_mask, double* keys, hipStream_t s) {
-    const int64_t blocks = (int64_t)p.W * p.n_c;
-    if (blocks == 0) return hipSuccess;
+    // a 2-D grid: W * n_c workgroups would exceed the 32-bit work-item count
+    // of a 1-D dispatch at the plan limits
+    if (p.W == 0 || p.n_c == 0) return hipSuccess;
     const bool f16 = p.dtype == GA_FP16;
     const int32_t n_c = (int32_t)p.n_c;
-#define GA_NORM_LAUNCH(F, Z)                                                                             \
-    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z>), dim3((unsigned)blocks), dim3(kNormThreads), \
-                       0, s, bucket, layer_ptrs, p.d_offsets, p.L, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, \
-                       keys)
+#define GA_NORM_LAUNCH(F, Z)                                                                               \
+    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z>), dim3((unsigned)p.n_c, (unsigned)p.W),   \
+                       dim3(kNormThreads), 0, s, bucket, layer_ptrs, p.d_offsets, p.L, resid, p.ld, p.P, p.C, \
+                       n_c, prev_mask, p.mw, keys)
     if (f16 && prev_mask) GA_NORM_LAUNCH(true, true);
     else if (f16) GA_NORM_LAUNCH(true, false);
     else if (prev_mask) GA_NORM_LAUNCH(false, true);

@@ -64,6 +64,9 @@ extern "C" {
 #define GA_ABI_VERSION 1
 #define GA_MAX_WORKERS 1024
 #define GA_MAX_CHUNKS 65536
+/* Most elements per worker (P) of a plan or an SGD call: every 1-D grid of
+   4 or more elements per thread then stays within 2^31 work-items. */
+#define GA_MAX_ELEMENTS ((int64_t)1 << 33)
 
 typedef enum {
     GA_OK = 0,
@@ -113,7 +116,9 @@ const char* ga_last_error(void);
  * chunk = 0 makes a dense-only plan; chunk >= 1 adds the sparse sizes with
  *   n_c = ceil(P / chunk) and k = min(n_c, ceil(keep_ratio * n_c - 1e-9)),
  *   i.e. the fewest chunks that are at least the keep ratio of all chunks.
- * Limits: 1 <= W <= GA_MAX_WORKERS, n_c <= GA_MAX_CHUNKS, 0 <= keep_ratio <= 1.
+ * Limits: 1 <= W <= GA_MAX_WORKERS, P <= GA_MAX_ELEMENTS, n_c <= GA_MAX_CHUNKS,
+ * 0 <= keep_ratio <= 1; beyond them GA_ERR_UNSUPPORTED (sizes) or
+ * GA_ERR_INVALID (W, keep_ratio).
  */
 ga_status ga_plan_compute_info(int32_t W, int32_t n_layers, const int64_t* layer_numel,
                                ga_dtype grad_dtype, int64_t chunk, double keep_ratio,
@@ -291,7 +296,8 @@ ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64
  * Momentum SGD on binary32 master weights, Caffe form (FireCaffe runs Caffe
  * models and reproduces Caffe's numbers [FC FAQ]), per element:
  *   v <- fl(fl(mu * v) + fl(lr * g));   w <- fl(w - v)
- * three roundings, no fused multiply-add, no weight decay.  P >= 0 elements.
+ * three roundings, no fused multiply-add, no weight decay.
+ * 0 <= P <= GA_MAX_ELEMENTS elements (GA_ERR_UNSUPPORTED above).
  */
 ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, float* d_v,
                                 const ga_sgd* sgd, hipStream_t stream);

@@ -130,6 +130,22 @@ def test_size_limits_are_inclusive(ga):
     assert e.value.status == ga.GA_ERR_UNSUPPORTED
 
 
+def test_element_limit(ga):
+    """P up to GA_MAX_ELEMENTS per worker (summed over layers), not one more;
+    the standalone SGD call has the same limit and checks it before any
+    pointer."""
+    half = ga.MAX_ELEMENTS // 2
+    info = ga.compute_info(ga.MAX_WORKERS, [half, half], False, 0, 0.0)
+    assert info.P == ga.MAX_ELEMENTS
+    for numels in ([ga.MAX_ELEMENTS + 1], [half, half, 1]):
+        with pytest.raises(ga.GAError) as e:
+            ga.compute_info(2, numels, True, 0, 0.0)
+        assert e.value.status == ga.GA_ERR_UNSUPPORTED
+    L = ga.lib()
+    s = ga.SGD(0.01, 0.9)
+    assert L.ga_sgd_momentum_apply(ga.MAX_ELEMENTS + 1, 16, 16, 16, ctypes.byref(s), None) == ga.GA_ERR_UNSUPPORTED
+
+
 def test_header_is_plain_c_and_client_links(ga):
     """include/gradagg.h compiles as C11 with gcc and a C program links against
     the library (the client itself runs in the GPU tests)."""

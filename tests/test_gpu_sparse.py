@@ -218,3 +218,16 @@ def test_sparse_maximum_worker_count(ga):
     wl = workloads.custom(ga.MAX_WORKERS, [3000, 77], True, sigma=1e-3, scale_mode="chunk",
                           scale_log10=(-4.0, 0.0), chunk=256, rho=0.25)
     run_sparse(ga, wl, steps=2, lazy=True)
+
+
+def test_sparse_both_limits(ga):
+    """W and n_c both at the library's limits (1024 workers x 65536 chunks of
+    8 elements, the last one ragged): 2^26 (worker, chunk) pairs, more
+    workgroups than a 1-D grid of 256-thread groups can address.  One step
+    (the oracle takes about half a minute for it)."""
+    n_c = ga.MAX_CHUNKS
+    wl = workloads.custom(ga.MAX_WORKERS, [8 * (n_c - 1) + 5], True, sigma=1e-3, scale_mode="chunk",
+                          scale_log10=(-4.0, 0.0), chunk=8, rho=0.1)
+    print("W=%d n_c=%d P=%d" % (wl.W, n_c, wl.P), flush=True)
+    res = run_sparse(ga, wl, steps=1, lazy=False)
+    assert res.keys.shape == (ga.MAX_WORKERS, n_c)
