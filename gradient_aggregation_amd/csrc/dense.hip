@@ -21,7 +21,12 @@ namespace ga {
 namespace {
 
 constexpr int kThreads = 256;
+// Leaves in flight per thread (U): 16 in general; 4 for binary16 leaves with
+// W >= 64, where 16 holds so many registers that only two wavefronts fit on a
+// SIMD (GoogLeNet W=128: 4 is 2-4% faster; AlexNet W=16: 16 is 7% faster).
 constexpr int kUnrollW = 16;
+constexpr int kUnrollNarrow = 4;
+constexpr int kNarrowMinW = 64;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -124,7 +129,7 @@ __device__ __forceinline__ void epilogue(const float (&s)[E], int64_t i0, int64_
     }
 }
 
-template <int LEV, bool FP16>
+template <int LEV, bool FP16, int U>
 __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ bucket, int64_t ld,
                                                    int32_t W, int64_t P, float invW,
                                                    float* __restrict__ grad, int32_t do_sgd, float lr,
@@ -142,13 +147,13 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
 
     TreeAcc<LEV, E> tree;
     uint32_t cnt = 0;
-    for (int32_t w0 = 0; w0 < W; w0 += kUnrollW) {
-        raw x[kUnrollW];
+    for (int32_t w0 = 0; w0 < W; w0 += U) {
+        raw x[U];
 #pragma unroll
-        for (int u = 0; u < kUnrollW; ++u)
+        for (int u = 0; u < U; ++u)
             if (w0 + u < W) x[u] = load_leaf(base + (int64_t)(w0 + u) * row_bytes);
 #pragma unroll
-        for (int u = 0; u < kUnrollW; ++u) {
+        for (int u = 0; u < U; ++u) {
             if (w0 + u < W) {
                 float f[E];
                 LV::widen(x[u], f);
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_tree(const void* __restrict__ buck
 // the layer once and reads each worker's tensor with 128-bit loads (element
 // loads when a tensor is not 16-byte aligned); a wavefront that straddles a
 // layer boundary resolves the layer of every element.
-template <int LEV, bool FP16>
+template <int LEV, bool FP16, int U>
 __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* __restrict__ layer_ptrs,
                                                   const int64_t* __restrict__ offsets,
                                                   const uint32_t* __restrict__ tile_layer,
@@ -244,22 +249,22 @@ __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* _
             const uint32_t mine_lo = (uint32_t)mine, mine_hi = (uint32_t)(mine >> 32);
             const int32_t gn = W - g0 < 64 ? W - g0 : 64;
             const int64_t byte_off = (i0 - off0) * kEsz;
-            for (int32_t u0 = 0; u0 < gn; u0 += kUnrollW) {
+            for (int32_t u0 = 0; u0 < gn; u0 += U) {
                 // All addresses first, then all loads with no branch between
-                // them, so the 16 loads are in flight together (past the group
+                // them, so the U loads are in flight together (past the group
                 // end the last worker is re-read and not pushed).
-                uint64_t addr[kUnrollW];
+                uint64_t addr[U];
 #pragma unroll
-                for (int u = 0; u < kUnrollW; ++u) {
+                for (int u = 0; u < U; ++u) {
                     const int ui = u0 + u < gn ? u0 + u : gn - 1;
                     addr[u] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine_hi, ui) << 32) |
                               (uint32_t)__builtin_amdgcn_readlane((int)mine_lo, ui);
                 }
-                raw x[kUnrollW];
+                raw x[U];
 #pragma unroll
-                for (int u = 0; u < kUnrollW; ++u) x[u] = load_leaf_at(addr[u] + (uint64_t)byte_off);
+                for (int u = 0; u < U; ++u) x[u] = load_leaf_at(addr[u] + (uint64_t)byte_off);
 #pragma unroll
-                for (int u = 0; u < kUnrollW; ++u) {
+                for (int u = 0; u < U; ++u) {
                     if (u0 + u < gn) {
                         float f[E];
                         LV::widen(x[u], f);
@@ -274,9 +279,9 @@ __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* _
         // tail, or meets an unaligned tensor): each lane resolves the layer of
         // its own first element and, when its E elements lie in that layer at
         // an E-aligned offset and the tensor is aligned, reads each worker
-        // with one 128-bit load, otherwise element by element; 8 workers in
-        // flight.
-        constexpr int kU = 8;
+        // with one 128-bit load, otherwise element by element; up to 8
+        // workers in flight.
+        constexpr int kU = U < 8 ? U : 8;
         const int32_t la = valid ? layer_of(i0) : 0;
         const int64_t oa = offsets[la], ea = offsets[la + 1];
         const bool lane_vec = valid && i0 + E <= ea && (oa % E) == 0;
@@ -327,7 +332,7 @@ __device__ __forceinline__ void tree_layers_block(int64_t blk, const uint64_t* _
 }
 
 // One workgroup per block of 256 * E elements.
-template <int LEV, bool FP16>
+template <int LEV, bool FP16, int U>
 __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __restrict__ layer_ptrs,
                                                           const int64_t* __restrict__ offsets,
                                                           const uint32_t* __restrict__ tile_layer,
@@ -337,13 +342,13 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers(const uint64_t* __rest
                                                           float* __restrict__ grad, int32_t do_sgd, float lr,
                                                           float mu, float* __restrict__ w,
                                                           float* __restrict__ v) {
-    tree_layers_block<LEV, FP16>(blockIdx.x, layer_ptrs, offsets, tile_layer, tile_order, n_tiles, L, tbl_stride,
+    tree_layers_block<LEV, FP16, U>(blockIdx.x, layer_ptrs, offsets, tile_layer, tile_order, n_tiles, L, tbl_stride,
                                  tbl_first, W, P, invW, grad, do_sgd, lr, mu, w, v);
 }
 
 // A capped grid (to leave compute units to a concurrent kernel): each
 // workgroup strides over the blocks.
-template <int LEV, bool FP16>
+template <int LEV, bool FP16, int U>
 __global__ __launch_bounds__(kThreads) void k_tree_layers_strided(const uint64_t* __restrict__ layer_ptrs,
                                                                   const int64_t* __restrict__ offsets,
                                                                   const uint32_t* __restrict__ tile_layer,
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_layers_strided(const uint64_t
                                                                   float mu, float* __restrict__ w,
                                                                   float* __restrict__ v) {
     for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x)
-        tree_layers_block<LEV, FP16>(blk, layer_ptrs, offsets, tile_layer, tile_order, n_tiles, L, tbl_stride,
+        tree_layers_block<LEV, FP16, U>(blk, layer_ptrs, offsets, tile_layer, tile_order, n_tiles, L, tbl_stride,
                                      tbl_first, W, P, invW, grad, do_sgd, lr, mu, w, v);
 }
 
@@ -384,20 +389,41 @@ __global__ __launch_bounds__(kThreads) void k_sgd(int64_t P, const float* __rest
     }
 }
 
-template <int LEV>
-hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
-                         float* v, hipStream_t s) {
-    const int E = p.dtype == GA_FP16 ? 8 : 4;
+template <int LEV, bool FP16, int U>
+hipError_t tree_launch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w, float* v,
+                       hipStream_t s) {
+    constexpr int E = FP16 ? 8 : 4;
     const int64_t threads = (p.P + E - 1) / E;
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
     const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
-    if (p.dtype == GA_FP16)
-        hipLaunchKernelGGL((k_tree<LEV, true>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W,
-                           p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+    hipLaunchKernelGGL((k_tree<LEV, FP16, U>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W, p.P, invW,
+                       grad, sgd ? 1 : 0, lr, mu, w, v);
+    return hipGetLastError();
+}
+
+template <int LEV>
+hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
+                         float* v, hipStream_t s) {
+    if constexpr (LEV == 8)
+        if (p.dtype == GA_FP16 && p.W >= kNarrowMinW)
+            return tree_launch<LEV, true, kUnrollNarrow>(p, bucket, grad, sgd, w, v, s);
+    if (p.dtype == GA_FP16) return tree_launch<LEV, true, kUnrollW>(p, bucket, grad, sgd, w, v, s);
+    return tree_launch<LEV, false, kUnrollW>(p, bucket, grad, sgd, w, v, s);
+}
+
+template <int LEV, bool FP16, int U>
+hipError_t tree_layers_launch(const Plan& p, const uint64_t* layer_ptrs, int32_t tbl_stride, int32_t tbl_first,
+                              int64_t n_blocks, int32_t max_blocks, float invW, float* grad, int do_sgd, float lr,
+                              float mu, float* w, float* v, hipStream_t s) {
+    if (max_blocks > 0 && max_blocks < n_blocks)
+        hipLaunchKernelGGL((k_tree_layers_strided<LEV, FP16, U>), dim3(max_blocks), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride, tbl_first, p.W,
+                           p.P, n_blocks, invW, grad, do_sgd, lr, mu, w, v);
     else
-        hipLaunchKernelGGL((k_tree<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W,
-                           p.P, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+        hipLaunchKernelGGL((k_tree_layers<LEV, FP16, U>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride, tbl_first, p.W,
+                           p.P, invW, grad, do_sgd, lr, mu, w, v);
     return hipGetLastError();
 }
 
@@ -411,25 +437,15 @@ hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, int32
     const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
     const int do_sgd = sgd ? 1 : 0;
-    if (max_blocks > 0 && max_blocks < n_blocks) {
-        if (p.dtype == GA_FP16)
-            hipLaunchKernelGGL((k_tree_layers_strided<LEV, true>), dim3(max_blocks), dim3(kThreads), 0, s,
-                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride,
-                               tbl_first, p.W, p.P, n_blocks, invW, grad, do_sgd, lr, mu, w, v);
-        else
-            hipLaunchKernelGGL((k_tree_layers_strided<LEV, false>), dim3(max_blocks), dim3(kThreads), 0, s,
-                               layer_ptrs, p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride,
-                               tbl_first, p.W, p.P, n_blocks, invW, grad, do_sgd, lr, mu, w, v);
-    } else if (p.dtype == GA_FP16) {
-        hipLaunchKernelGGL((k_tree_layers<LEV, true>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride, tbl_first, p.W,
-                           p.P, invW, grad, do_sgd, lr, mu, w, v);
-    } else {
-        hipLaunchKernelGGL((k_tree_layers<LEV, false>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.d_tile_order, p.n_tiles, p.L, tbl_stride, tbl_first, p.W,
-                           p.P, invW, grad, do_sgd, lr, mu, w, v);
-    }
-    return hipGetLastError();
+    if constexpr (LEV == 8)
+        if (p.dtype == GA_FP16 && p.W >= kNarrowMinW)
+            return tree_layers_launch<LEV, true, kUnrollNarrow>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks,
+                                                                max_blocks, invW, grad, do_sgd, lr, mu, w, v, s);
+    if (p.dtype == GA_FP16)
+        return tree_layers_launch<LEV, true, kUnrollW>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks, max_blocks,
+                                                       invW, grad, do_sgd, lr, mu, w, v, s);
+    return tree_layers_launch<LEV, false, kUnrollW>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks, max_blocks,
+                                                    invW, grad, do_sgd, lr, mu, w, v, s);
 }
 
 }  // namespace

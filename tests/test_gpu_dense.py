@@ -52,7 +52,7 @@ def run_dense(ga, wl, steps=2, pad_value=None, bucket_hook=None, want_grad=True,
     plan.close()
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 5, 7, 8, 16, 31, 32, 33, 127, 128, 129, 255, 256, 300, 1024])
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 7, 8, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 300, 1024])
 @pytest.mark.parametrize("fp16", [False, True])
 def test_dense_worker_counts(ga, W, fp16):
     P_layers = [1000, 3, 517] if W > 300 else [4096 * 7 + 5, 10, 999]

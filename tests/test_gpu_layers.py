@@ -25,7 +25,8 @@ def ga():
 
 @pytest.mark.parametrize("fp16", [False, True])
 @pytest.mark.parametrize("W,numels", [(1, [3]), (3, workloads.WORKLOADS["tiny"].numels),
-                                      (16, [8, 1, 5000, 7, 4096, 333]), (128, [2048, 10, 4099])])
+                                      (16, [8, 1, 5000, 7, 4096, 333]), (63, [4096, 1, 515]), (64, [777, 4096, 9]),
+                                      (128, [2048, 10, 4099])])
 @pytest.mark.parametrize("mis", list(MIS))
 def test_tree_reduce_layers(ga, fp16, W, numels, mis):
     wl = workloads.custom(W, numels, fp16, sigma=1e-2, scale_mode="layer")
