@@ -1,0 +1,91 @@
+"""Host-side checks of bench.py's helpers (no GPU): the one-GPU refusal, the
+byte counts of a deferred step from its two masks, and the rule that counter
+traffic is reported only for the kernel sources it was measured on."""
+import json
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def _mask(bits, W, n_c):
+    """[W][ceil(n_c/32)] int32 mask with bit c of worker w set for (w, c) in bits."""
+    import torch
+    mw = (n_c + 31) // 32
+    m = np.zeros((W, mw), np.uint32)
+    for w, c in bits:
+        m[w, c // 32] |= np.uint32(1) << np.uint32(c % 32)
+    return torch.from_numpy(m.view(np.int32))
+
+
+def test_deferred_bytes_brute_force():
+    """Counts and bytes against a direct loop over (worker, chunk), with a
+    ragged last chunk and chunks past bit 31 of a word."""
+    rng = np.random.default_rng(5)
+    W, C, n_c = 3, 256, 70
+    P = (n_c - 1) * C + 77
+    plan = types.SimpleNamespace(n_chunks=n_c, chunk=C)
+    prev = {(w, c) for w in range(W) for c in range(n_c) if rng.random() < 0.3}
+    cur = {(w, c) for w in range(W) for c in range(n_c) if rng.random() < 0.3}
+    prev |= {(0, n_c - 1)}
+    cur |= {(0, n_c - 1), (1, n_c - 1)}
+    got = bench.deferred_bytes(plan, _mask(prev, W, n_c), _mask(cur, W, n_c), P, 2)
+
+    def length(c):
+        return C if c < n_c - 1 else P - (n_c - 1) * C
+
+    resent = prev & cur
+    new = cur - prev
+    mat = prev - cur
+    assert got["chunks_resent"] == len(resent)
+    assert got["chunks_new"] == len(new)
+    assert got["chunks_materialized"] == len(mat)
+    assert got["gather_bytes"] == sum(length(c) for _, c in resent) * 2 + sum(length(c) for _, c in new) * 4 + 16 * P
+    assert got["materialize_bytes"] == sum(length(c) for _, c in mat) * 6
+
+
+def test_traffic_needs_the_profiled_sources(tmp_path):
+    """A counter record is returned while its sources hash as recorded, and not
+    once one of them changes or is missing."""
+    import hashlib
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    rel = os.path.relpath(str(src), bench.ROOT)
+    rec = {"k_x": {"bytes_per_launch": 123, "sources": [rel],
+                   "sources_sha256": hashlib.sha256(b"kernel v1\n").hexdigest(), "summary": "s.md"}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(rec))
+    assert bench.measured_traffic(str(path), "k_x")["bytes_per_launch"] == 123
+    assert bench.measured_traffic(str(path), "k_other") is None
+    src.write_text("kernel v2\n")
+    assert bench.measured_traffic(str(path), "k_x") is None
+    src.unlink()
+    assert bench.measured_traffic(str(path), "k_x") is None
+    assert bench.measured_traffic(str(tmp_path / "absent.json"), "k_x") is None
+
+
+@pytest.mark.parametrize("name", ["alexnet128_sparse", "googlenet", "alexnet16", "nin"])
+def test_committed_traffic_matches_current_sources(name):
+    """Every committed counter record still describes the kernel sources in
+    the tree, so bench.py reports its traffic."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    with open(path) as f:
+        keys = list(json.load(f))
+    assert keys
+    for k in keys:
+        assert bench.measured_traffic(path, k) is not None, (name, k)
