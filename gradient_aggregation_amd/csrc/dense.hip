@@ -23,7 +23,8 @@ namespace {
 constexpr int kThreads = 256;
 // Leaves in flight per thread (U): 16 in general; 4 for binary16 leaves with
 // W >= 64, where 16 holds so many registers that only two wavefronts fit on a
-// SIMD (GoogLeNet W=128: 4 is 2-4% faster; AlexNet W=16: 16 is 7% faster).
+// SIMD (4 is 2-4% faster at W = 128, 300 and 512; at W = 16, where a thread
+// reads all its leaves in one round, 16 is 7% faster).
 constexpr int kUnrollW = 16;
 constexpr int kUnrollNarrow = 4;
 constexpr int kNarrowMinW = 64;
@@ -405,10 +406,11 @@ hipError_t tree_launch(const Plan& p, const void* bucket, float* grad, const ga_
 template <int LEV>
 hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
                          float* v, hipStream_t s) {
+    // the 11-level tree serves W >= 256, so its binary16 form is always narrow
+    if (p.dtype == GA_FP16 && (LEV > 8 || p.W >= kNarrowMinW))
+        return tree_launch<LEV, true, kUnrollNarrow>(p, bucket, grad, sgd, w, v, s);
     if constexpr (LEV == 8)
-        if (p.dtype == GA_FP16 && p.W >= kNarrowMinW)
-            return tree_launch<LEV, true, kUnrollNarrow>(p, bucket, grad, sgd, w, v, s);
-    if (p.dtype == GA_FP16) return tree_launch<LEV, true, kUnrollW>(p, bucket, grad, sgd, w, v, s);
+        if (p.dtype == GA_FP16) return tree_launch<LEV, true, kUnrollW>(p, bucket, grad, sgd, w, v, s);
     return tree_launch<LEV, false, kUnrollW>(p, bucket, grad, sgd, w, v, s);
 }
 
@@ -437,13 +439,13 @@ hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, int32
     const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
     const int do_sgd = sgd ? 1 : 0;
+    if (p.dtype == GA_FP16 && (LEV > 8 || p.W >= kNarrowMinW))
+        return tree_layers_launch<LEV, true, kUnrollNarrow>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks,
+                                                            max_blocks, invW, grad, do_sgd, lr, mu, w, v, s);
     if constexpr (LEV == 8)
-        if (p.dtype == GA_FP16 && p.W >= kNarrowMinW)
-            return tree_layers_launch<LEV, true, kUnrollNarrow>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks,
-                                                                max_blocks, invW, grad, do_sgd, lr, mu, w, v, s);
-    if (p.dtype == GA_FP16)
-        return tree_layers_launch<LEV, true, kUnrollW>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks, max_blocks,
-                                                       invW, grad, do_sgd, lr, mu, w, v, s);
+        if (p.dtype == GA_FP16)
+            return tree_layers_launch<LEV, true, kUnrollW>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks,
+                                                           max_blocks, invW, grad, do_sgd, lr, mu, w, v, s);
     return tree_layers_launch<LEV, false, kUnrollW>(p, layer_ptrs, tbl_stride, tbl_first, n_blocks, max_blocks,
                                                     invW, grad, do_sgd, lr, mu, w, v, s);
 }
