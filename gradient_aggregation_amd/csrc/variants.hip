@@ -25,6 +25,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 16;
+// The tree keeps 4 binary16 leaves in flight for W >= 64 (16 would leave room
+// for only two wavefronts per SIMD), as the main tree kernel does.
+constexpr int kUnrollNarrow = 4;
+constexpr int kNarrowMinW = 64;
 
 // One 128-bit vector of a worker's row: loaded raw (4 VGPRs) and widened to
 // binary32 only when it is added.
@@ -89,7 +93,7 @@ __device__ __forceinline__ void mean_sgd(float (&s)[E], bool wire, int64_t i0, i
     }
 }
 
-template <int LEV, bool FP16, bool WIRE>
+template <int LEV, bool FP16, bool WIRE, int U>
 __global__ __launch_bounds__(kThreads) void k_variant_tree(const void* __restrict__ bucket, int64_t ld, int32_t W,
                                                            int64_t P, float invW, float* __restrict__ grad,
                                                            int32_t do_sgd, float lr, float mu,
@@ -102,13 +106,13 @@ __global__ __launch_bounds__(kThreads) void k_variant_tree(const void* __restric
     const char* base = static_cast<const char*>(bucket);
     TreeAcc<LEV, E, WIRE> tree;
     uint32_t cnt = 0;
-    for (int32_t w0 = 0; w0 < W; w0 += kUnroll) {
-        u32x4 x[kUnroll];
+    for (int32_t w0 = 0; w0 < W; w0 += U) {
+        u32x4 x[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             if (w0 + u < W) x[u] = load_raw(base + ((int64_t)(w0 + u) * ld + i0) * esz);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             if (w0 + u < W) {
                 float f[E];
                 V::widen(x[u], f);
@@ -178,12 +182,16 @@ hipError_t launch_variant_typed(const Plan& p, const void* bucket, int order, fl
     const int do_sgd = sgd ? 1 : 0;
     const int64_t Q = ((p.P + p.W - 1) / p.W + 63) / 64 * 64;
     if (order == GA_ORDER_TREE) {
-        if (p.W < (1 << 8))
-            hipLaunchKernelGGL((k_variant_tree<8, FP16, WIRE>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W,
-                               p.P, invW, grad, do_sgd, lr, mu, w, v);
-        else
-            hipLaunchKernelGGL((k_variant_tree<11, FP16, WIRE>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld,
+        constexpr int UW = FP16 ? kUnrollNarrow : kUnroll;  // leaves in flight for W >= 64
+        if (p.W >= (1 << 8))
+            hipLaunchKernelGGL((k_variant_tree<11, FP16, WIRE, UW>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld,
                                p.W, p.P, invW, grad, do_sgd, lr, mu, w, v);
+        else if (p.W >= kNarrowMinW)
+            hipLaunchKernelGGL((k_variant_tree<8, FP16, WIRE, UW>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld,
+                               p.W, p.P, invW, grad, do_sgd, lr, mu, w, v);
+        else
+            hipLaunchKernelGGL((k_variant_tree<8, FP16, WIRE, kUnroll>), dim3(blocks), dim3(kThreads), 0, s, bucket,
+                               p.ld, p.W, p.P, invW, grad, do_sgd, lr, mu, w, v);
     } else if (order == GA_ORDER_SERVER) {
         hipLaunchKernelGGL((k_variant_seq<FP16, WIRE, false>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld,
                            p.W, p.P, Q, invW, grad, do_sgd, lr, mu, w, v);
