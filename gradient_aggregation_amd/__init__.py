@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.ga_sparse_gather_reduce.restype = st
         L.ga_sparse_gather_reduce.argtypes = [_VP, _VP, _VP, ctypes.c_int32, _VP, ctypes.POINTER(SGD), _VP, _VP,
                                               _VP]
+        L.ga_tree_partial.restype = st
+        L.ga_tree_partial.argtypes = [_VP, _VP, _VP, _VP]
+        L.ga_tree_combine.restype = st
+        L.ga_tree_combine.argtypes = [_VP, _VP, ctypes.c_int32, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
         L.ga_sgd_momentum_apply.restype = st
         L.ga_sgd_momentum_apply.argtypes = [ctypes.c_int64, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP]
         L.ga_chunk_norm_layers_defer.restype = st
@@ -248,6 +252,25 @@ class Plan:
                                     _dev(grad, torch.float32, self.P, "grad"), sgd,
                                     _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
                                     _stream_ptr()))
+
+    def tree_partial(self, bucket, out) -> None:
+        """Unscaled tree sum S of the W rows of bucket into out ([P] float32):
+        one GPU's part of the dense step split across GPUs."""
+        torch = _torch()
+        _check(lib().ga_tree_partial(self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),
+                                     _dev(out, torch.float32, self.P, "out"), _stream_ptr()))
+
+    def tree_combine(self, partials, w_total: int, grad=None, w=None, v=None, lr: Optional[float] = None,
+                     mu: Optional[float] = None) -> None:
+        """The owner's step of the split dense step: the tree over the W rows of
+        partials ([W][ld] float32, this plan binary32), mean over w_total
+        workers, SGD on this slice."""
+        torch = _torch()
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_tree_combine(self._h, _dev(partials, torch.float32, self.W * self.ld, "partials"),
+                                     int(w_total), _dev(grad, torch.float32, self.P, "grad"), sgd,
+                                     _dev(w, torch.float32, self.P, "w"), _dev(v, torch.float32, self.P, "v"),
+                                     _stream_ptr()))
 
     def tree_reduce_layers(self, layer_ptrs, grad=None, w=None, v=None, lr: Optional[float] = None,
                            mu: Optional[float] = None) -> None:

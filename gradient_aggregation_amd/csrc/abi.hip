@@ -382,6 +382,34 @@ ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const 
         "sparse_gather_reduce launch");
 }
 
+ga_status ga_tree_partial(const ga_plan* plan, const void* d_bucket, float* d_sum, hipStream_t stream) {
+    if (!plan || !d_bucket || !d_sum) return fail(GA_ERR_INVALID, "NULL argument");
+    if (!aligned16(d_bucket) || !aligned16(d_sum)) return fail(GA_ERR_ALIGN, "device buffers must be 16-byte aligned");
+    const ga::Plan* p = as_plan(plan);
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    // S * 1.0f is S, bit for bit
+    return device_status(ga::launch_tree_scaled(*p, d_bucket, 1.0f, d_sum, nullptr, nullptr, nullptr, stream),
+                         "tree_partial launch");
+}
+
+ga_status ga_tree_combine(const ga_plan* plan, const float* d_partials, int32_t w_total, float* d_grad,
+                          const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream) {
+    if (!plan || !d_partials) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->dtype != GA_FP32) return fail(GA_ERR_INVALID, "partial sums are binary32: the plan must be GA_FP32");
+    if (w_total < 1) return fail(GA_ERR_INVALID, "w_total=%d < 1", w_total);
+    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
+    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
+    if (!aligned16(d_partials) || (d_grad && !aligned16(d_grad)) || (sgd && (!aligned16(d_w) || !aligned16(d_v))))
+        return fail(GA_ERR_ALIGN, "device buffers must be 16-byte aligned");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_tree_scaled(*p, d_partials, (float)(1.0 / (double)w_total), d_grad, sgd, d_w,
+                                                d_v, stream),
+                         "tree_combine launch");
+}
+
 ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, float* d_v, const ga_sgd* sgd,
                                 hipStream_t stream) {
     if (P < 0 || !sgd) return fail(GA_ERR_INVALID, "bad size or NULL sgd");

@@ -391,12 +391,11 @@ __global__ __launch_bounds__(kThreads) void k_sgd(int64_t P, const float* __rest
 }
 
 template <int LEV, bool FP16, int U>
-hipError_t tree_launch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w, float* v,
-                       hipStream_t s) {
+hipError_t tree_launch(const Plan& p, const void* bucket, float invW, float* grad, const ga_sgd* sgd, float* w,
+                       float* v, hipStream_t s) {
     constexpr int E = FP16 ? 8 : 4;
     const int64_t threads = (p.P + E - 1) / E;
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-    const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
     hipLaunchKernelGGL((k_tree<LEV, FP16, U>), dim3(blocks), dim3(kThreads), 0, s, bucket, p.ld, p.W, p.P, invW,
                        grad, sgd ? 1 : 0, lr, mu, w, v);
@@ -404,14 +403,14 @@ hipError_t tree_launch(const Plan& p, const void* bucket, float* grad, const ga_
 }
 
 template <int LEV>
-hipError_t tree_dispatch(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
+hipError_t tree_dispatch(const Plan& p, const void* bucket, float invW, float* grad, const ga_sgd* sgd, float* w,
                          float* v, hipStream_t s) {
     // the 11-level tree serves W >= 256, so its binary16 form is always narrow
     if (p.dtype == GA_FP16 && (LEV > 8 || p.W >= kNarrowMinW))
-        return tree_launch<LEV, true, kUnrollNarrow>(p, bucket, grad, sgd, w, v, s);
+        return tree_launch<LEV, true, kUnrollNarrow>(p, bucket, invW, grad, sgd, w, v, s);
     if constexpr (LEV == 8)
-        if (p.dtype == GA_FP16) return tree_launch<LEV, true, kUnrollW>(p, bucket, grad, sgd, w, v, s);
-    return tree_launch<LEV, false, kUnrollW>(p, bucket, grad, sgd, w, v, s);
+        if (p.dtype == GA_FP16) return tree_launch<LEV, true, kUnrollW>(p, bucket, invW, grad, sgd, w, v, s);
+    return tree_launch<LEV, false, kUnrollW>(p, bucket, invW, grad, sgd, w, v, s);
 }
 
 template <int LEV, bool FP16, int U>
@@ -454,11 +453,16 @@ hipError_t tree_layers_dispatch(const Plan& p, const uint64_t* layer_ptrs, int32
 
 hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd, float* w,
                        float* v, hipStream_t s) {
+    return launch_tree_scaled(p, bucket, (float)(1.0 / (double)p.W), grad, sgd, w, v, s);
+}
+
+hipError_t launch_tree_scaled(const Plan& p, const void* bucket, float scale, float* grad, const ga_sgd* sgd,
+                              float* w, float* v, hipStream_t s) {
     if (p.P == 0) return hipSuccess;
     // Eight levels for every W below 256: measured no slower than a shallower
     // tree for small W (fewer resident waves, same bytes in flight).
-    if (p.W < (1 << 8)) return tree_dispatch<8>(p, bucket, grad, sgd, w, v, s);
-    return tree_dispatch<11>(p, bucket, grad, sgd, w, v, s);
+    if (p.W < (1 << 8)) return tree_dispatch<8>(p, bucket, scale, grad, sgd, w, v, s);
+    return tree_dispatch<11>(p, bucket, scale, grad, sgd, w, v, s);
 }
 
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,

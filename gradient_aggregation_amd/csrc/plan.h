@@ -35,6 +35,9 @@ ga_status api_ok();
 // ---- launchers (each returns hipSuccess or the launch error) -------------
 hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_sgd* sgd,
                        float* w, float* v, hipStream_t s);
+// launch_tree with g = S * scale instead of S * fl32(1/W).
+hipError_t launch_tree_scaled(const Plan& p, const void* bucket, float scale, float* grad, const ga_sgd* sgd,
+                              float* w, float* v, hipStream_t s);
 hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid,
                              const uint32_t* prev_mask, double* keys, hipStream_t s);
 hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, float* resid,

@@ -303,6 +303,36 @@ ga_status ga_sgd_momentum_apply(int64_t P, const float* d_grad, float* d_w, floa
                                 const ga_sgd* sgd, hipStream_t stream);
 
 /*
+ * The dense step split across G GPUs, as each GPU would run its part [FC
+ * sec. 6: the reduction tree spans the nodes; its lower levels are local].
+ * With W workers in G groups of m = W/G consecutive workers (m a power of
+ * two), the W-worker tree T(0, W) is the G-leaf tree over the groups'
+ * complete subtrees T(j*m, m), so
+ *   1. every GPU sums its own m workers: ga_tree_partial;
+ *   2. a reduce-scatter hands the owner of an element slice the G partial
+ *      sums of that slice, one row per group in group order;
+ *   3. the owner adds them in the tree's order, takes the mean over all W
+ *      workers and applies SGD to its slice: ga_tree_combine;
+ * and the result is bit for bit that of ga_tree_reduce over all W workers.
+ *
+ * ga_tree_partial: S[i] = T(0, W) over the plan's W rows of d_bucket (as in
+ *   ga_tree_reduce), stored unscaled in d_sum ([P] binary32, 16-byte aligned).
+ *   No mean, no SGD.
+ */
+ga_status ga_tree_partial(const ga_plan* plan, const void* d_bucket, float* d_sum, hipStream_t stream);
+
+/*
+ * ga_tree_combine: the owner's step.  plan: a binary32 plan with W = G rows
+ * and the slice's length as its element count.  d_partials: [G][ld] binary32,
+ * row j = group j's partial sums for the slice.  w_total: the number of
+ * workers the partials stand for (>= 1); the mean is S * fl32(1/w_total).
+ * d_grad, sgd, d_w, d_v: as in ga_tree_reduce, for the slice.
+ * GA_ERR_INVALID for a binary16 plan or w_total < 1.
+ */
+ga_status ga_tree_combine(const ga_plan* plan, const float* d_partials, int32_t w_total, float* d_grad,
+                          const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream);
+
+/*
  * Multi-bucket lazy allreduce [GF]: lazy allreduce fuses the layers' gradients
  * into buckets, and aggregation of a bucket overlaps with the computation of
  * the layers not yet produced.  A backward pass writes the last layer first,

@@ -95,6 +95,8 @@ def test_calls_reject_null_plan_without_launching(ga):
     assert L.ga_reduce_variant(None, None, 0, 0, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_tree_reduce_layers(None, None, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_chunk_norm_layers(None, None, None, None, None, None) == ga.GA_ERR_INVALID
+    assert L.ga_tree_partial(None, None, None, None) == ga.GA_ERR_INVALID
+    assert L.ga_tree_combine(None, None, 1, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_sgd_momentum_apply(-1, None, None, None, None, None) == ga.GA_ERR_INVALID
     s = ga.SGD(0.01, 0.9)
     assert L.ga_sgd_momentum_apply(0, None, None, None, ctypes.byref(s), None) == ga.GA_OK
