@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--producer-batch", type=int, default=64,
                     help="--overlap gemm: samples per worker; a layer's weight-gradient GEMM reduces over "
                          "batch x output positions")
+    ap.add_argument("--split", type=int, default=0,
+                    help="time the two per-GPU kernels of the dense step split across this many GPUs (W/G "
+                         "workers each): one GPU's partial tree sum and one owner's combine of G partials")
     ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the "
                                                     "dominant kernel (from rocprofv3 counters); default: "
                                                     "profiles/traffic_<workload>.json")
@@ -136,6 +139,9 @@ def main():
         return
     if args.overlap:
         run_overlap(args)
+        return
+    if args.split:
+        run_split(args)
         return
 
     wl = workloads.WORKLOADS[args.workload]
@@ -553,6 +559,63 @@ def run_overlap(args):
         "buckets": rows,
     }
     print(json.dumps(result), flush=True)
+
+
+def run_split(args):
+    """The per-GPU kernels of the dense step split across G GPUs, at their
+    real shapes: ga_tree_partial over one GPU's W/G workers (all P elements)
+    and ga_tree_combine over the G partial rows of one owner's slice of
+    ceil(P/G) elements (mean and SGD included).  The exchange between them
+    (a reduce-scatter of P*4 bytes per GPU) is not run; its bytes are given."""
+    import torch
+    import gradient_aggregation_amd as ga
+    import workloads
+    wl = workloads.WORKLOADS[args.workload]
+    W, G, P = wl.W, args.split, wl.P
+    m = W // G if G > 0 else 0
+    if G < 1 or m * G != W or m & (m - 1):
+        print("--split G needs W/G a power of two (W=%d)" % W, file=sys.stderr)
+        sys.exit(2)
+    gdt = torch.float16 if wl.fp16 else torch.float32
+    torch.manual_seed(3)
+    grp = ga.Plan(m, wl.numels, wl.fp16)
+    bucket = (torch.randn((m, grp.ld), device="cuda") * 1e-3).to(gdt)
+    part_out = torch.empty(P, dtype=torch.float32, device="cuda")
+    Q = ((P + G - 1) // G + 63) // 64 * 64
+    own = ga.Plan(G, [Q], False)
+    partials = torch.randn((G, own.ld), device="cuda") * 1e-3
+    g = torch.empty(Q, dtype=torch.float32, device="cuda")
+    w = torch.randn(Q, device="cuda") * 0.05
+    v = torch.zeros(Q, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    steps = args.steps or 200
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    t_part = timed(lambda: grp.tree_partial(bucket, part_out))
+    t_comb = timed(lambda: own.tree_combine(partials, W, None, w, v, wl.lr, wl.mu))
+    b_in = 2 if wl.fp16 else 4
+    part_bytes = m * P * b_in + 4 * P
+    comb_bytes = G * Q * 4 + 16 * Q
+    xchg = (G - 1) * ((P + G - 1) // G) * 4
+    print(json.dumps({
+        "metric": "per-GPU kernels of the dense step split across GPUs", "workload": wl.name, "W": W, "G": G,
+        "workers_per_gpu": m, "P": P, "slice": Q, "steps": steps,
+        "partial_ms": round(t_part, 4), "partial_GBps": round(part_bytes / (t_part * 1e-3) / 1e9, 1),
+        "combine_ms": round(t_comb, 4), "combine_GBps": round(comb_bytes / (t_comb * 1e-3) / 1e9, 1),
+        "exchange_bytes_per_gpu": xchg,
+        "exchange_ms_at_7_links_153GBps": round(xchg / (7 * 153e9) * 1e3, 4),
+        "data": "synthetic"}), flush=True)
 
 
 def time_pack(plan, wl, src, layer_tensors, stream):
