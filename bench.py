@@ -699,26 +699,34 @@ def measured_traffic(path, kernel):
     return rec if h.hexdigest() == rec["sources_sha256"] else None
 
 
-def cpu_baseline(wl, plan, host_bucket, w_init, thr):
-    """The oracle, as it is, timed on the host cores: one whole step of the
-    workload (all W workers) on the first gradient batch."""
+def cpu_baseline(wl, plan, host_bucket, w_init, thr, min_s=10.0, max_steps=5):
+    """The oracle, as it is, timed on the host cores: whole steps of the
+    workload (all W workers) on the first gradient batch, repeated until at
+    least `min_s` seconds of work (at most `max_steps` steps); the sparse
+    residual and the w, v state carry over from step to step."""
     import oracle
     P = wl.P
     b_in = 2 if wl.fp16 else 4
     sparse = wl.mode == "sparse"
     w = w_init.copy()
     v = np.zeros(P, np.float32)
-    t = time.time()
-    if sparse:
-        r = np.zeros(host_bucket.shape, np.float32)
-        oracle.sparse_step(host_bucket, P, wl.fp16, wl.chunk, plan.k, r, wl.lr, wl.mu, w, v, want_keys=False,
-                           want_gbar=False, threads=thr)
-        del r
-    else:
-        oracle.dense_step(host_bucket, P, wl.fp16, wl.lr, wl.mu, w, v, want_gbar=False, threads=thr)
-    t = time.time() - t
+    r = np.zeros(host_bucket.shape, np.float32) if sparse else None
+    steps = 0
+    t0 = time.time()
+    while True:
+        if sparse:
+            oracle.sparse_step(host_bucket, P, wl.fp16, wl.chunk, plan.k, r, wl.lr, wl.mu, w, v,
+                               want_keys=False, want_gbar=False, threads=thr)
+        else:
+            oracle.dense_step(host_bucket, P, wl.fp16, wl.lr, wl.mu, w, v, want_gbar=False, threads=thr)
+        steps += 1
+        if time.time() - t0 >= min_s or steps >= max_steps:
+            break
+    total = time.time() - t0
+    del r
+    t = total / steps
     b_alg = wl.W * P * ((b_in + 8) if sparse else b_in) + 16 * P
-    log("cpu baseline: oracle step over all %d workers in %.2fs on %d threads" % (wl.W, t, thr))
+    log("cpu baseline: %d oracle steps over all %d workers in %.2fs on %d threads" % (steps, wl.W, total, thr))
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -730,8 +738,9 @@ def cpu_baseline(wl, plan, host_bucket, w_init, thr):
         pass
     return {"value": round(b_alg / t / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
             "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
-            "sample": "one whole %s step of the workload (all %d workers, P=%d), first gradient batch, "
-                      "oracle threads=%d, %.2f s" % (wl.mode, wl.W, P, thr, t)}
+            "sample": "%d consecutive whole %s steps of the workload (all %d workers, P=%d) on the first "
+                      "gradient batch, oracle threads=%d, %.2f s in all, %.2f s per step"
+                      % (steps, wl.mode, wl.W, P, thr, total, t)}
 
 
 if __name__ == "__main__":
