@@ -4,9 +4,11 @@
 Default workload: AlexNet-shaped, W=128 workers x P=60,965,224 parameters,
 binary16 gradients, coarse-grained sparse communication with 32768-element
 chunks keeping 10% of them per worker (k=187 of 1861), the residual carried in
-lazy-zero mode (deferred form by default: a chunk sent in the previous step
-stores no a, and the gather reads its gradient), and momentum SGD on binary32
-master weights.
+lazy-zero mode (by default in its deferred, pending form: a chunk sent in the
+previous step stores no a and the gather reads its gradient; if it is not sent
+again, its residual stays held as that gradient, which the next step's norm
+pass reads, so the previous step's gradient tensors are kept one step), and
+momentum SGD on binary32 master weights.
 
 One step = lazy-allreduce fusion of the W*16 per-layer gradient tensors read
 with zero copy through the layer table, together with the chunk norms and the
@@ -23,7 +25,7 @@ Prints one JSON line:
   roofline         the dominant kernel (k_chunk_norm): 10*W*P bytes per launch
                    over its mean launch time from HIP events on its stream,
                    against the 8 TB/s HBM peak
-  cpu_baseline     the oracle timed on the host cores, one whole step
+  cpu_baseline     the oracle timed on the host cores over whole steps
 """
 from __future__ import annotations
 
@@ -57,9 +59,11 @@ def parse():
     ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
     ap.add_argument("--source", choices=["layers", "bucket"], default="layers",
                     help="gradients as per-layer tensors fused with zero copy (default) or a packed bucket")
-    ap.add_argument("--residual", choices=["deferred", "lazy"], default="deferred",
+    ap.add_argument("--residual", choices=["pending", "deferred", "lazy"], default="pending",
                     help="sparse workload: lazy-zero residual with one mask buffer, or its deferred form (chunks "
-                         "sent in the previous step store no a; the gather reads their gradient)")
+                         "sent in the previous step store no a; the gather reads their gradient), or the pending "
+                         "form of that (the residual of a chunk sent in the previous step but not now stays held "
+                         "as the step's gradient, which the next step's norm pass reads)")
     ap.add_argument("--order", choices=["tree", "server", "ring"], default="tree",
                     help="dense workloads: summation order (parameter server, ring) for comparison")
     ap.add_argument("--wire", choices=["f32", "f16"], default="f32",
@@ -212,7 +216,7 @@ def main():
     gen_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
-    defer = False
+    defer = pending = False
     if sparse:
         rd = plan.empty_residual()
         keys = plan.empty_keys()
@@ -220,7 +224,8 @@ def main():
         mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
         # deferred mode: two mask buffers swap roles (previous / current step)
         masks = [mask, torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")]
-        defer = args.residual == "deferred" and layers_src and plan.chunk % 256 == 0
+        defer = args.residual in ("deferred", "pending") and layers_src and plan.chunk % 256 == 0
+        pending = defer and args.residual == "pending"
         names = ["chunk_norm", "topk", "gather_sgd"]
     else:
         names = ["tree_sgd"]
@@ -235,13 +240,21 @@ def main():
             e[0].record(stream)
         if sparse and defer:
             prev, cur = masks[t % 2], masks[(t + 1) % 2]
-            plan.chunk_norm_layers_defer(b, rd, keys, prev)
+            if pending:
+                # cur still holds the mask of two steps back; the previous
+                # step's gradient tensors are those of the previous batch
+                plan.chunk_norm_layers_pending(b, sources[(t - 1) % nb] if t > 0 else b, rd, keys, prev, cur)
+            else:
+                plan.chunk_norm_layers_defer(b, rd, keys, prev)
             if rec:
                 e[1].record(stream)
             plan.chunk_topk(keys, idx, cur)
             if rec:
                 e[2].record(stream)
-            plan.sparse_gather_reduce_layers_defer(b, rd, prev, cur, None, wd, vd, wl.lr, wl.mu)
+            if pending:
+                plan.sparse_gather_reduce_layers_pending(b, rd, prev, cur, None, wd, vd, wl.lr, wl.mu)
+            else:
+                plan.sparse_gather_reduce_layers_defer(b, rd, prev, cur, None, wd, vd, wl.lr, wl.mu)
             if rec:
                 e[3].record(stream)
         elif sparse:
@@ -296,6 +309,11 @@ def main():
 
     b_in = 2 if wl.fp16 else 4
     deferred_last = deferred_bytes(plan, masks[(n_steps - 1) % 2], masks[n_steps % 2], P, b_in) if defer else None
+    if pending:
+        # nothing is materialized: those chunks' residuals stay pending and
+        # the next norm pass reads them as gradient (b_in per element)
+        deferred_last["chunks_pending"] = deferred_last.pop("chunks_materialized")
+        deferred_last["pending_read_bytes_next_step"] = deferred_last.pop("materialize_bytes") // (b_in + 4) * b_in
 
     pack = time_pack(plan, wl, sources[-1], keep[-1] if layers_src else None, stream)
 
@@ -323,7 +341,7 @@ def main():
         else "k_variant_" + ("tree" if args.order == "tree" else "seq")
     traffic_key = dom_kernel if not variant else "%s_order_%s_wire_%s" % (dom_kernel, args.order, args.wire)
     if defer:
-        traffic_key = dom_kernel + "_deferred"
+        traffic_key = dom_kernel + ("_pending" if pending else "_deferred")
     traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
                                traffic_key)
 
@@ -346,7 +364,8 @@ def main():
             "accumulate": "f32 fixed binary tree", "keys": "f64" if sparse else None,
             "chunk": plan.chunk or None, "keep_ratio": wl.rho if sparse else None,
             "k": plan.k if sparse else None, "n_chunks": plan.n_chunks if sparse else None,
-            "residual_mode": ("deferred lazy-zero" if defer else "lazy-zero") if sparse else None,
+            "residual_mode": (("pending deferred lazy-zero" if pending else "deferred lazy-zero") if defer
+                              else "lazy-zero") if sparse else None,
             "gradient_batches": nb,
             "fusion": "zero-copy read of %d per-layer tensors" % (W * len(wl.numels)) if layers_src
                       else "pre-packed bucket",

@@ -100,6 +100,13 @@ def lib() -> ctypes.CDLL:
         L.ga_sparse_gather_reduce_layers_defer.restype = st
         L.ga_sparse_gather_reduce_layers_defer.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP,
                                                            _VP, _VP]
+        L.ga_chunk_norm_layers_pending.restype = st
+        L.ga_chunk_norm_layers_pending.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_sparse_gather_reduce_layers_pending.restype = st
+        L.ga_sparse_gather_reduce_layers_pending.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(SGD),
+                                                             _VP, _VP, _VP]
+        L.ga_residual_flush_layers.restype = st
+        L.ga_residual_flush_layers.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
         L.ga_bucket_boundaries.restype = st
         L.ga_bucket_boundaries.argtypes = [ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP]
         L.ga_buckets_create.restype = st
@@ -328,6 +335,46 @@ class Plan:
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
             _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
             _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
+
+    def chunk_norm_layers_pending(self, layer_ptrs, prev_layer_ptrs, resid, keys, prev_mask, prev2_mask) -> None:
+        """Pending-residual chunk norms: as chunk_norm_layers_defer, and chunks
+        set in prev2_mask but not in prev_mask take the previous step's
+        gradient (prev_layer_ptrs) + 0 as their residual."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        _check(lib().ga_chunk_norm_layers_pending(
+            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+            _dev(prev_layer_ptrs, torch.int64, self.W * L, "prev_layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+            _dev(prev2_mask, torch.int32, self.W * self.mask_words, "prev2_mask"),
+            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
+
+    def sparse_gather_reduce_layers_pending(self, layer_ptrs, resid, prev_mask, sel_mask, grad=None, w=None,
+                                            v=None, lr: Optional[float] = None, mu: Optional[float] = None) -> None:
+        """The deferred gather-reduce without writing the residual of chunks
+        sent in the previous step but not now (it stays pending)."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_sparse_gather_reduce_layers_pending(
+            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
+            _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
+            _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
+
+    def residual_flush_layers(self, layer_ptrs, resid, prev_mask, sel_mask) -> None:
+        """Write the pending residuals of a step (chunks set in prev_mask but
+        not in sel_mask get the widened gradient + 0)."""
+        torch = _torch()
+        L = len(self.layer_numels)
+        _check(lib().ga_residual_flush_layers(
+            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
+            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
 
     def chunk_norm(self, bucket, resid, keys, prev_mask=None) -> None:
         torch = _torch()

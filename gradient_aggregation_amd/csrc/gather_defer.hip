@@ -15,6 +15,9 @@
 //   - and writes the residual of a chunk sent in the previous step but not now
 //     (the widened gradient), so that afterwards the residual buffer holds
 //     exactly what the non-deferred lazy mode leaves (k_materialize).
+// In the pending form the last part is left out: that residual stays held as
+// the step's gradient, which the next step's norm pass reads in its place;
+// launch_residual_flush writes it when the buffer itself is wanted.
 #include "device.h"
 #include "plan.h"
 #include "tree.h"
@@ -387,10 +390,27 @@ __global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __rest
     }
 }
 
+// k_materialize over every (worker, mask word): the residual of each chunk
+// set in prev_mask but not in sel_mask becomes the widened gradient + 0.
+hipError_t materialize_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resid,
+                                const uint32_t* prev_mask, const uint32_t* sel_mask, hipStream_t s) {
+    const int64_t words = (int64_t)p.W * p.mw * kMatParts;
+    if (words == 0) return hipSuccess;
+    if (p.dtype == GA_FP16)
+        hipLaunchKernelGGL((k_materialize<true>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
+                           prev_mask, sel_mask, p.mw);
+    else
+        hipLaunchKernelGGL((k_materialize<false>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
+                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
+                           prev_mask, sel_mask, p.mw);
+    return hipGetLastError();
+}
+
 template <int LEV>
 hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
                           const uint32_t* sel_mask, float* grad, const ga_sgd* sgd, float* w, float* v,
-                          hipStream_t s) {
+                          bool materialize, hipStream_t s) {
     const int64_t threads = (p.P + 3) / 4;
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
     const float invW = (float)(1.0 / (double)p.W);
@@ -404,30 +424,29 @@ hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resi
                            p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask,
                            sel_mask, p.mw, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !materialize) return e;
     // the (worker, chunk) pairs written here are disjoint from those the
     // reduction reads, so the order of the two launches does not matter
-    const int64_t words = (int64_t)p.W * p.mw * kMatParts;
-    if (p.dtype == GA_FP16)
-        hipLaunchKernelGGL((k_materialize<true>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
-                           prev_mask, sel_mask, p.mw);
-    else
-        hipLaunchKernelGGL((k_materialize<false>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
-                           prev_mask, sel_mask, p.mw);
-    return hipGetLastError();
+    return materialize_dispatch(p, layer_ptrs, resid, prev_mask, sel_mask, s);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
                                       const uint32_t* prev_mask, const uint32_t* sel_mask, float* grad,
-                                      const ga_sgd* sgd, float* w, float* v, hipStream_t s) {
+                                      const ga_sgd* sgd, float* w, float* v, bool materialize, hipStream_t s) {
     if (p.P == 0) return hipSuccess;
-    if (p.W < (1 << 5)) return defer_dispatch<5>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
-    if (p.W < (1 << 8)) return defer_dispatch<8>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
-    return defer_dispatch<11>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, s);
+    if (p.W < (1 << 5))
+        return defer_dispatch<5>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, materialize, s);
+    if (p.W < (1 << 8))
+        return defer_dispatch<8>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, materialize, s);
+    return defer_dispatch<11>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, materialize, s);
+}
+
+hipError_t launch_residual_flush(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
+                                 const uint32_t* sel_mask, hipStream_t s) {
+    if (p.P == 0) return hipSuccess;
+    return materialize_dispatch(p, layer_ptrs, resid, prev_mask, sel_mask, s);
 }
 
 }  // namespace ga

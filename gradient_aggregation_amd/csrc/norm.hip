@@ -11,7 +11,10 @@
 // with cross-lane moves, then across the 4 wavefronts through LDS.  Traffic
 // per worker-element: 2 B (binary16 gradient) + 4 B (residual read) + 4 B
 // (residual write); in lazy-zero mode the residual of a chunk sent in the
-// previous step is taken as zero and not read.
+// previous step is taken as zero and not read.  In the pending form the residual of a
+// chunk sent two steps ago but not in the previous step is still held as the
+// previous step's gradient (it was that gradient plus +0) and is read from
+// those tensors: 2 B per binary16 element instead of 4.
 #include "device.h"
 #include "plan.h"
 
@@ -113,6 +116,64 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
     }
 }
 
+// Flat elements [ss, se) of one worker whose residual is pending: it is the
+// previous step's gradient plus +0 (a chunk sent two steps ago, so its
+// residual was zero, and not sent in the previous step), read from that
+// step's tensor psrc at the same offsets as the gradient src.  a = leaf +
+// residual is stored.  With vec_ok, both tensors are 16-byte aligned at ss.
+template <bool FP16>
+__device__ __forceinline__ void norm_segment_pending(gptr<void> __restrict__ src, gptr<void> __restrict__ psrc,
+                                                     int64_t soff, bool vec_ok, float* __restrict__ r, int64_t ss,
+                                                     int64_t se, double& acc0, double& acc1) {
+    constexpr int UN = 4;
+    const int64_t nvec = vec_ok ? (se - ss) >> 3 : 0;
+    int64_t j = threadIdx.x;
+    for (; j < nvec; j += UN * kNormThreads) {
+        float lf[UN][8], pf[UN][8];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int64_t i = ss + ((j + u * kNormThreads) << 3);
+            if (j + u * kNormThreads >= nvec) continue;
+            if (FP16) {
+                widen8(load_u4(static_cast<gptr<uint16_t>>(src) + (i - soff)), lf[u]);
+                widen8(load_u4(static_cast<gptr<uint16_t>>(psrc) + (i - soff)), pf[u]);
+            } else {
+                gptr<float> gp = static_cast<gptr<float>>(src) + (i - soff);
+                gptr<float> pp = static_cast<gptr<float>>(psrc) + (i - soff);
+                const float4 g0 = load_f4(gp), g1 = load_f4(gp + 4);
+                const float4 p0 = load_f4(pp), p1 = load_f4(pp + 4);
+                lf[u][0] = g0.x; lf[u][1] = g0.y; lf[u][2] = g0.z; lf[u][3] = g0.w;
+                lf[u][4] = g1.x; lf[u][5] = g1.y; lf[u][6] = g1.z; lf[u][7] = g1.w;
+                pf[u][0] = p0.x; pf[u][1] = p0.y; pf[u][2] = p0.z; pf[u][3] = p0.w;
+                pf[u][4] = p1.x; pf[u][5] = p1.y; pf[u][6] = p1.z; pf[u][7] = p1.w;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            if (j + u * kNormThreads >= nvec) continue;
+            const int64_t i = ss + ((j + u * kNormThreads) << 3);
+            float a[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                a[q] = lf[u][q] + (pf[u][q] + 0.f);
+                if (q & 1) acc1 = fma((double)a[q], (double)a[q], acc1);
+                else acc0 = fma((double)a[q], (double)a[q], acc0);
+            }
+            *reinterpret_cast<float4*>(r + i) = make_float4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<float4*>(r + i + 4) = make_float4(a[4], a[5], a[6], a[7]);
+        }
+    }
+    for (int64_t i = ss + (nvec << 3) + threadIdx.x; i < se; i += kNormThreads) {
+        const float lf = FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i - soff])
+                              : static_cast<gptr<float>>(src)[i - soff];
+        const float pf = FP16 ? widen1(static_cast<gptr<uint16_t>>(psrc)[i - soff])
+                              : static_cast<gptr<float>>(psrc)[i - soff];
+        const float a = lf + (pf + 0.f);
+        r[i] = a;
+        acc0 = fma((double)a, (double)a, acc0);
+    }
+}
+
 // One workgroup per (worker w = blockIdx.y, chunk c = blockIdx.x).  LAYERS: the gradient is read from
 // the W*L per-layer tensors of the layer table (zero-copy fusion: the chunk's
 // elements are gathered from the layers it overlaps); otherwise from the
@@ -121,11 +182,15 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
 // computes its key but does not store a, which is the widened gradient; the
 // deferred gather reads the gradient for it instead, and writes it as the
 // residual if the chunk is not sent again.
-template <bool FP16, bool LAZY, bool LAYERS, bool DEFER = false>
+// PEND (with DEFER): a chunk set in prev2_mask (sent two steps ago) but not
+// in prev_mask has the previous step's gradient as its residual, read from
+// prev_layer_ptrs (the previous step's layer table) instead of resid.
+template <bool FP16, bool LAZY, bool LAYERS, bool DEFER = false, bool PEND = false>
 __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     const void* __restrict__ bucket, const uint64_t* __restrict__ layer_ptrs,
     const int64_t* __restrict__ offsets, int32_t L, float* __restrict__ resid, int64_t ld, int64_t P,
-    int64_t C, int32_t n_c, const uint32_t* __restrict__ prev_mask, int32_t mw, double* __restrict__ keys) {
+    int64_t C, int32_t n_c, const uint32_t* __restrict__ prev_mask, int32_t mw, double* __restrict__ keys,
+    const uint64_t* __restrict__ prev_layer_ptrs, const uint32_t* __restrict__ prev2_mask) {
     const int32_t w = (int32_t)blockIdx.y;
     const int32_t c = (int32_t)blockIdx.x;
     const int64_t b = (int64_t)w * n_c + c;
@@ -133,6 +198,8 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     const int64_t e = s + C < P ? s + C : P;
     bool rzero = false;
     if (LAZY) rzero = (prev_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
+    bool pend = false;
+    if (PEND && !rzero) pend = (prev2_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
 
     float* __restrict__ r = resid + (int64_t)w * ld;
     double acc0 = 0.0, acc1 = 0.0;
@@ -148,10 +215,15 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
             const int64_t off = offsets[l], end = offsets[l + 1];
             const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
             const bool vec_ok = (off & 7) == 0 && (addr & 15) == 0;
-            if (DEFER && rzero)
+            if (DEFER && rzero) {
                 norm_segment<FP16, false>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s,
                                           end < e ? end : e, rzero, acc0, acc1);
-            else
+            } else if (PEND && pend) {
+                const uint64_t paddr = prev_layer_ptrs[(int64_t)w * L + l];
+                norm_segment_pending<FP16>(as_global<void>(addr), as_global<void>(paddr), off,
+                                           vec_ok && (paddr & 15) == 0, r, off > s ? off : s, end < e ? end : e,
+                                           acc0, acc1);
+            } else
                 norm_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e,
                                    rzero, acc0, acc1);
         }
@@ -173,18 +245,20 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     }
 }
 
-template <bool LAYERS, bool DEFER = false>
+template <bool LAYERS, bool DEFER = false, bool PEND = false>
 hipError_t norm_dispatch(const Plan& p, const void* bucket, const uint64_t* layer_ptrs, float* resid,
-                         const uint32_t* prev_mask, double* keys, hipStream_t s) {
+                         const uint32_t* prev_mask, double* keys, hipStream_t s,
+                         const uint64_t* prev_layer_ptrs = nullptr, const uint32_t* prev2_mask = nullptr) {
     // a 2-D grid: W * n_c workgroups would exceed the 32-bit work-item count
     // of a 1-D dispatch at the plan limits
     if (p.W == 0 || p.n_c == 0) return hipSuccess;
     const bool f16 = p.dtype == GA_FP16;
     const int32_t n_c = (int32_t)p.n_c;
 #define GA_NORM_LAUNCH(F, Z)                                                                               \
-    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z>), dim3((unsigned)p.n_c, (unsigned)p.W),   \
-                       dim3(kNormThreads), 0, s, bucket, layer_ptrs, p.d_offsets, p.L, resid, p.ld, p.P, p.C, \
-                       n_c, prev_mask, p.mw, keys)
+    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z, PEND && Z>),                                \
+                       dim3((unsigned)p.n_c, (unsigned)p.W), dim3(kNormThreads), 0, s, bucket, layer_ptrs,     \
+                       p.d_offsets, p.L, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys, prev_layer_ptrs,  \
+                       prev2_mask)
     if (f16 && prev_mask) GA_NORM_LAUNCH(true, true);
     else if (f16) GA_NORM_LAUNCH(true, false);
     else if (prev_mask) GA_NORM_LAUNCH(false, true);
@@ -208,6 +282,14 @@ hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, f
 hipError_t launch_chunk_norm_layers_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
                                           const uint32_t* prev_mask, double* keys, hipStream_t s) {
     return norm_dispatch<true, true>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s);
+}
+
+hipError_t launch_chunk_norm_layers_pending(const Plan& p, const uint64_t* layer_ptrs,
+                                            const uint64_t* prev_layer_ptrs, float* resid,
+                                            const uint32_t* prev_mask, const uint32_t* prev2_mask, double* keys,
+                                            hipStream_t s) {
+    return norm_dispatch<true, true, true>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s, prev_layer_ptrs,
+                                           prev2_mask);
 }
 
 }  // namespace ga

@@ -46,12 +46,24 @@ hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, f
 // sent in the previous step does not store its a.
 hipError_t launch_chunk_norm_layers_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
                                           const uint32_t* prev_mask, double* keys, hipStream_t s);
+// launch_chunk_norm_layers_defer, and a chunk set in prev2_mask but not in
+// prev_mask takes the previous step's gradient (prev_layer_ptrs) + 0 as its
+// residual.
+hipError_t launch_chunk_norm_layers_pending(const Plan& p, const uint64_t* layer_ptrs,
+                                            const uint64_t* prev_layer_ptrs, float* resid,
+                                            const uint32_t* prev_mask, const uint32_t* prev2_mask, double* keys,
+                                            hipStream_t s);
 // Gather-reduce for deferred mode: a chunk sent now and in the previous step
-// is read from the gradient tensors; one sent before but not now gets its
-// residual (the widened gradient) written.  C must be a multiple of 256.
+// is read from the gradient tensors; with materialize, one sent before but not
+// now gets its residual (the widened gradient) written.  C must be a multiple
+// of 256.
 hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
                                       const uint32_t* prev_mask, const uint32_t* sel_mask, float* grad,
-                                      const ga_sgd* sgd, float* w, float* v, hipStream_t s);
+                                      const ga_sgd* sgd, float* w, float* v, bool materialize, hipStream_t s);
+// The residual of every chunk set in prev_mask but not in sel_mask becomes
+// the widened gradient (layer_ptrs) + 0.
+hipError_t launch_residual_flush(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
+                                 const uint32_t* sel_mask, hipStream_t s);
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
 // launch_tree_layers over a sub-list of layers: worker w's layer l is entry

@@ -293,6 +293,62 @@ ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64
                                                hipStream_t stream);
 
 /*
+ * Pending-residual form of the deferred step [GF]: the residual of a chunk a
+ * worker sent in step t-1 but not in step t is, after step t, that worker's
+ * widened step-t gradient + 0 (a was the gradient plus a zero residual).  It
+ * is not written at step t: the norm pass of step t+1 reads it from the
+ * step-t gradient tensors (2 B per binary16 element instead of a 4 B write
+ * and a 4 B read).  The caller therefore keeps each step's gradient tensors,
+ * unchanged, until the next step's norm pass has run (for example, two
+ * gradient buffers per worker used in turn).  One step t is
+ *   ga_chunk_norm_layers_pending(cur layers, prev layers, prev, prev2) ->
+ *   ga_chunk_topk(into prev2's buffer) ->
+ *   ga_sparse_gather_reduce_layers_pending(cur layers, prev, cur)
+ * with the same two mask buffers as the deferred form: prev holds step t-1's
+ * mask and the other buffer still holds step t-2's when the norm pass reads
+ * it as prev2, before the top-k overwrites it with step t's.  The first step
+ * passes all-zero masks (and any valid layer table as prev layers).  Keys,
+ * selection, mean gradient, w and v are those of the lazy-zero sequence, bit
+ * for bit.
+ *
+ * ga_chunk_norm_layers_pending: as ga_chunk_norm_layers_defer, and a chunk set
+ *   in d_prev2_mask but not in d_prev_mask takes d_prev_layer_ptrs' widened
+ *   gradient + 0 as its residual (d_residual is not read there); a is stored.
+ *   d_prev_layer_ptrs: [W*L] device addresses of the previous step's tensors,
+ *   laid out as d_layer_ptrs.  Errors as ga_chunk_norm_layers_defer.
+ */
+ga_status ga_chunk_norm_layers_pending(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                       const uint64_t* d_prev_layer_ptrs, float* d_residual,
+                                       const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask, double* d_keys,
+                                       hipStream_t stream);
+
+/*
+ * ga_sparse_gather_reduce_layers_pending: ga_sparse_gather_reduce_layers_defer
+ * without the residual write of the chunks set in d_prev_mask but not in
+ * d_sel_mask.  Afterwards d_residual holds the new residual except on those
+ * chunks, whose residual is the widened gradient of d_layer_ptrs + 0 (written
+ * by the next ga_chunk_norm_layers_pending, or by ga_residual_flush_layers).
+ * Arguments and errors as ga_sparse_gather_reduce_layers_defer.
+ */
+ga_status ga_sparse_gather_reduce_layers_pending(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                                 float* d_residual, const uint32_t* d_prev_mask,
+                                                 const uint32_t* d_sel_mask, float* d_grad, const ga_sgd* sgd,
+                                                 float* d_w, float* d_v, hipStream_t stream);
+
+/*
+ * ga_residual_flush_layers: writes the pending residuals of a step, so that
+ * d_residual holds the whole residual (before a checkpoint, at the end of
+ * training, or before the step's gradient tensors are reused): for every
+ * chunk set in d_prev_mask but not in d_sel_mask, d_residual = the widened
+ * gradient of d_layer_ptrs + 0.  Pass the step's layer table and its two
+ * masks, as given to ga_sparse_gather_reduce_layers_pending.  Writing them is
+ * harmless to the next pending step, which computes the same values itself.
+ * Errors: GA_ERR_INVALID (NULL, dense-only plan), GA_ERR_ALIGN, GA_ERR_DEVICE.
+ */
+ga_status ga_residual_flush_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
+                                   const uint32_t* d_prev_mask, const uint32_t* d_sel_mask, hipStream_t stream);
+
+/*
  * Momentum SGD on binary32 master weights, Caffe form (FireCaffe runs Caffe
  * models and reproduces Caffe's numbers [FC FAQ]), per element:
  *   v <- fl(fl(mu * v) + fl(lr * g));   w <- fl(w - v)

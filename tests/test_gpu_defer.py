@@ -2,7 +2,11 @@
 for chunks sent in the previous step; a gather that reads the gradient tensors
 for chunks sent twice in a row and writes the residual of chunks sent before
 but not now) against the oracle over consecutive steps, and bit for bit
-against the plain lazy-zero sequence on the GPU."""
+against the plain lazy-zero sequence on the GPU.  The pending form (that
+residual left as the step's gradient, read by the next step's norm pass, and
+written on demand by the flush) is checked the same way: its residual through
+a flushed copy, so the steps themselves never see a flush, and once more with
+the live buffer flushed after every step."""
 import numpy as np
 import pytest
 
@@ -32,7 +36,7 @@ def sent_elements(mask, C, P, n_c):
     return np.repeat(sent, C, axis=1)[:, :P]
 
 
-def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False):
+def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False, mode="defer"):
     C, P = wl.chunk, wl.P
     plan = ga.Plan(wl.W, wl.numels, wl.fp16, chunk=C, keep_ratio=wl.rho)
     ld, k, n_c = plan.ld, plan.k, plan.n_chunks
@@ -44,7 +48,8 @@ def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False):
     idx = torch.full((wl.W, max(k, 1)), -1, dtype=torch.int32, device="cuda")
     masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(2)]
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
-    print("[defer] W=%d P=%d fp16=%s C=%d rho=%g %s" % (wl.W, P, wl.fp16, C, wl.rho, mis), flush=True)
+    print("[%s] W=%d P=%d fp16=%s C=%d rho=%g %s" % (mode, wl.W, P, wl.fp16, C, wl.rho, mis), flush=True)
+    prev_layers = None      # the previous step's tensors, kept alive for the pending form
     for step in range(1, steps + 1):
         b = workloads.grad_bucket(wl, step, ld)
         if hook is not None:
@@ -52,9 +57,23 @@ def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False):
         res = oracle.sparse_step(b, P, wl.fp16, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         cur, prev = masks[step % 2], masks[(step + 1) % 2]
         buf, ptrs = device_layers(b[:, :P], wl.numels, MIS[mis])
-        plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
-        plan.chunk_topk(keys, idx, cur)
-        plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        r_view = rd
+        if mode == "defer":
+            plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        else:
+            # cur still holds the mask of two steps back (all zero at first)
+            pptrs = ptrs if prev_layers is None else prev_layers[1]
+            plan.chunk_norm_layers_pending(ptrs, pptrs, rd, keys, prev, cur)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+            if mode == "pending_flush":
+                plan.residual_flush_layers(ptrs, rd, prev, cur)
+            else:
+                r_view = rd.clone()
+                plan.residual_flush_layers(ptrs, r_view, prev, cur)
+            prev_layers = (buf, ptrs)
         torch.cuda.synchronize()
         if wl.rho not in (0.0, 1.0):
             assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
@@ -62,7 +81,7 @@ def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False):
         if k > 0:
             assert np.array_equal(host(idx)[:, :k], res.sel_idx), "selected chunk indices differ"
         assert np.array_equal(host(cur).view(np.uint32), res.sel_mask)
-        r_got = host(rd)[:, :P].copy()
+        r_got = host(r_view)[:, :P].copy()
         r_got[sent_elements(host(cur), C, P, n_c)] = 0.0
         same = assert_same_bits
         if strict:
@@ -86,10 +105,31 @@ def test_defer_matches_oracle(ga, fp16, W, numels, C, mis):
     run_defer(ga, wl, mis)
 
 
+@pytest.mark.parametrize("fp16", [False, True])
+@pytest.mark.parametrize("W,numels,C", [(1, [3000, 7, 2000], 256), (3, workloads.WORKLOADS["tiny"].numels, 512),
+                                        (16, [8, 1, 5000, 7, 4096, 333, 64], 256), (33, [20000, 37, 4003], 1024),
+                                        (128, [2048, 16, 4099, 520], 256), (300, [3000, 17, 1000], 512)])
+@pytest.mark.parametrize("mis", list(MIS))
+def test_pending_matches_oracle(ga, fp16, W, numels, C, mis):
+    wl = workloads.custom(W, numels, fp16, sigma=1e-3, scale_mode="chunk", scale_log10=(-4.0, 0.0), chunk=C,
+                          rho=0.2)
+    run_defer(ga, wl, mis, steps=5, mode="pending")
+
+
+@pytest.mark.parametrize("fp16", [False, True])
+def test_pending_flushed_every_step(ga, fp16):
+    """Flushing the live residual after every step changes nothing: the next
+    norm pass computes the same pending values itself."""
+    wl = workloads.custom(16, [8, 1, 5000, 7, 4096, 333, 64], fp16, sigma=1e-3, scale_mode="chunk",
+                          scale_log10=(-4.0, 0.0), chunk=256, rho=0.2)
+    run_defer(ga, wl, "mixed", steps=5, mode="pending_flush")
+
+
+@pytest.mark.parametrize("mode", ["defer", "pending"])
 @pytest.mark.parametrize("rho", [0.0, 1.0])
-def test_defer_keep_ratio_extremes(ga, rho):
+def test_defer_keep_ratio_extremes(ga, rho, mode):
     wl = workloads.custom(6, [9000, 11, 300], True, sigma=1e-2, chunk=256, rho=rho)
-    run_defer(ga, wl, "mixed", steps=3)
+    run_defer(ga, wl, "mixed", steps=3, mode=mode)
 
 
 def test_defer_negative_zero_leaves(ga):
@@ -98,10 +138,11 @@ def test_defer_negative_zero_leaves(ga):
     def hook(b, step):
         b[:, 100:300] = 0x8000          # binary16 -0 in every worker
         b[1:, 600:700] = 0x8000
-    wl = workloads.custom(4, [3000], True, sigma=1e-2, chunk=256, rho=1.0)
-    run_defer(ga, wl, "aligned", steps=3, hook=hook, strict=True)
-    wl = workloads.custom(4, [3000], True, sigma=1e-2, chunk=256, rho=0.5)
-    run_defer(ga, wl, "aligned", steps=3, hook=hook, strict=True)
+    for mode in ("defer", "pending"):
+        wl = workloads.custom(4, [3000], True, sigma=1e-2, chunk=256, rho=1.0)
+        run_defer(ga, wl, "aligned", steps=3, hook=hook, strict=True, mode=mode)
+        wl = workloads.custom(4, [3000], True, sigma=1e-2, chunk=256, rho=0.5)
+        run_defer(ga, wl, "aligned", steps=4, hook=hook, strict=True, mode=mode)
 
 
 def test_defer_errors(ga):
@@ -119,4 +160,12 @@ def test_defer_errors(ga):
     with pytest.raises(ga.GAError) as e:
         plan.sparse_gather_reduce_layers_defer(ptrs, rd, m0, m0, g)
     assert e.value.status == ga.GA_ERR_INVALID
+    with pytest.raises(ga.GAError) as e:
+        plan.sparse_gather_reduce_layers_pending(ptrs, rd, m0, m0, g)
+    assert e.value.status == ga.GA_ERR_INVALID
+    plan = ga.Plan(4, [1000], True, chunk=64, keep_ratio=0.5)
+    rd = plan.empty_residual()
+    with pytest.raises(ga.GAError) as e:
+        plan.sparse_gather_reduce_layers_pending(ptrs, rd, m0, m1, g)
+    assert e.value.status == ga.GA_ERR_UNSUPPORTED
 

@@ -148,10 +148,12 @@ def test_buckets_alexnet16_full_size(ga, cap):
         log("alexnet16 buckets (cap %d) step %d ok in %.1fs" % (cap, step, time.time() - t0))
 
 
-def test_sparse_alexnet128_full_size_deferred(ga):
-    """The AlexNet-shaped W=128 sparse workload as benchmarked by default: 2048
-    per-layer tensors, 3 consecutive steps in deferred lazy-zero mode (two
-    mask buffers), every output compared with the oracle."""
+@pytest.mark.parametrize("mode,steps", [("defer", 3), ("pending", 4)])
+def test_sparse_alexnet128_full_size_deferred(ga, mode, steps):
+    """The AlexNet-shaped W=128 sparse workload as benchmarked: 2048 per-layer
+    tensors, consecutive steps in deferred lazy-zero mode (two mask buffers)
+    or its pending form (the previous step's tensors kept; the residual is
+    compared through a flushed copy), every output compared with the oracle."""
     wl = workloads.WORKLOADS["alexnet128_sparse"]
     C = wl.chunk
     plan = ga.Plan(wl.W, wl.numels, True, chunk=C, keep_ratio=wl.rho)
@@ -167,16 +169,27 @@ def test_sparse_alexnet128_full_size_deferred(ga):
     masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(2)]
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
     sample = [0, 1, 63, 127]
-    for step in (1, 2, 3):
+    prev_layers = None
+    for step in range(1, steps + 1):
         t0 = time.time()
         b = workloads.grad_bucket(wl, step, ld, seg=seg)
         buf, ptrs = device_layers(b[:, :P], wl.numels)
         res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         del b
         prev, cur = masks[(step + 1) % 2], masks[step % 2]
-        plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
-        plan.chunk_topk(keys, idx, cur)
-        plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        r_view = rd
+        if mode == "defer":
+            plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        else:
+            pptrs = ptrs if prev_layers is None else prev_layers[1]
+            plan.chunk_norm_layers_pending(ptrs, pptrs, rd, keys, prev, cur)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+            r_view = rd.clone()
+            plan.residual_flush_layers(ptrs, r_view, prev, cur)
+            prev_layers = (buf, ptrs)
         torch.cuda.synchronize()
         del buf
         assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
@@ -188,9 +201,10 @@ def test_sparse_alexnet128_full_size_deferred(ga):
         assert_same_bits(host(vd), v_ref, "v")
         m = host(cur).view(np.uint32)
         for w in sample:
-            r = host(rd[w, :P]).copy()
+            r = host(r_view[w, :P]).copy()
             for c in range(n_c):
                 if (int(m[w, c >> 5]) >> (c & 31)) & 1:
                     r[c * C:min((c + 1) * C, P)] = 0.0
             assert_same_bits(r, r_ref[w, :P], "residual of worker %d" % w)
-        log("deferred step %d compared in %.1fs" % (step, time.time() - t0))
+        del r_view
+        log("%s step %d compared in %.1fs" % (mode, step, time.time() - t0))
