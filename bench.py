@@ -4,11 +4,12 @@
 Default workload: AlexNet-shaped, W=128 workers x P=60,965,224 parameters,
 binary16 gradients, coarse-grained sparse communication with 32768-element
 chunks keeping 10% of them per worker (k=187 of 1861), the residual carried in
-lazy-zero mode (by default in its deferred, pending form: a chunk sent in the
-previous step stores no a and the gather reads its gradient; if it is not sent
-again, its residual stays held as that gradient, which the next step's norm
-pass reads, so the previous step's gradient tensors are kept one step), and
-momentum SGD on binary32 master weights.
+lazy-zero mode (by default in its deferred, depth-2 pending form: a chunk
+sent in the previous step stores no a and the gather reads its gradient; if it
+is not sent again, its residual stays held as that gradient, and one step
+later as the sum of the two gradients, which the next passes recompute; so the
+gradient tensors of the previous two steps are kept), and momentum SGD on
+binary32 master weights.
 
 One step = lazy-allreduce fusion of the W*16 per-layer gradient tensors read
 with zero copy through the layer table, together with the chunk norms and the
@@ -59,11 +60,12 @@ def parse():
     ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
     ap.add_argument("--source", choices=["layers", "bucket"], default="layers",
                     help="gradients as per-layer tensors fused with zero copy (default) or a packed bucket")
-    ap.add_argument("--residual", choices=["pending", "deferred", "lazy"], default="pending",
+    ap.add_argument("--residual", choices=["pending2", "pending", "deferred", "lazy"], default="pending2",
                     help="sparse workload: lazy-zero residual with one mask buffer, or its deferred form (chunks "
                          "sent in the previous step store no a; the gather reads their gradient), or the pending "
                          "form of that (the residual of a chunk sent in the previous step but not now stays held "
-                         "as the step's gradient, which the next step's norm pass reads)")
+                         "as the step's gradient, which the next step's norm pass reads), or its depth-2 form (a chunk pending one "
+                         "step stores no a either; the previous two gradient batches are kept)")
     ap.add_argument("--order", choices=["tree", "server", "ring"], default="tree",
                     help="dense workloads: summation order (parameter server, ring) for comparison")
     ap.add_argument("--wire", choices=["f32", "f16"], default="f32",
@@ -216,7 +218,7 @@ def main():
     gen_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
-    defer = pending = False
+    defer = pending = pending2 = False
     if sparse:
         rd = plan.empty_residual()
         keys = plan.empty_keys()
@@ -224,8 +226,11 @@ def main():
         mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
         # deferred mode: two mask buffers swap roles (previous / current step)
         masks = [mask, torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")]
-        defer = args.residual in ("deferred", "pending") and layers_src and plan.chunk % 256 == 0
-        pending = defer and args.residual == "pending"
+        defer = args.residual in ("deferred", "pending", "pending2") and layers_src and plan.chunk % 256 == 0
+        pending = defer and args.residual in ("pending", "pending2")
+        pending2 = defer and args.residual == "pending2"
+        if pending2:
+            masks.append(torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda"))
         names = ["chunk_norm", "topk", "gather_sgd"]
     else:
         names = ["tree_sgd"]
@@ -238,7 +243,22 @@ def main():
         e = ev[t]
         if rec:
             e[0].record(stream)
-        if sparse and defer:
+        if sparse and pending2:
+            # three mask buffers in turn (cur holds the mask of three steps
+            # back); the gradient tensors of the previous two batches
+            cur, prev, prev2 = masks[t % 3], masks[(t + 2) % 3], masks[(t + 1) % 3]
+            g1 = sources[(t - 1) % nb] if t > 0 else b
+            g2 = sources[(t - 2) % nb] if t > 1 else b
+            plan.chunk_norm_layers_pending2(b, g1, g2, rd, keys, prev, prev2, cur)
+            if rec:
+                e[1].record(stream)
+            plan.chunk_topk(keys, idx, cur)
+            if rec:
+                e[2].record(stream)
+            plan.sparse_gather_reduce_layers_pending2(b, g1, rd, prev, cur, prev2, None, wd, vd, wl.lr, wl.mu)
+            if rec:
+                e[3].record(stream)
+        elif sparse and defer:
             prev, cur = masks[t % 2], masks[(t + 1) % 2]
             if pending:
                 # cur still holds the mask of two steps back; the previous
@@ -308,7 +328,11 @@ def main():
         ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
 
     b_in = 2 if wl.fp16 else 4
-    deferred_last = deferred_bytes(plan, masks[(n_steps - 1) % 2], masks[n_steps % 2], P, b_in) if defer else None
+    if pending2:
+        tl = n_steps - 1
+        deferred_last = deferred_bytes(plan, masks[(tl + 2) % 3], masks[tl % 3], P, b_in)
+    else:
+        deferred_last = deferred_bytes(plan, masks[(n_steps - 1) % 2], masks[n_steps % 2], P, b_in) if defer else None
     if pending:
         # nothing is materialized: those chunks' residuals stay pending and
         # the next norm pass reads them as gradient (b_in per element)
@@ -341,7 +365,7 @@ def main():
         else "k_variant_" + ("tree" if args.order == "tree" else "seq")
     traffic_key = dom_kernel if not variant else "%s_order_%s_wire_%s" % (dom_kernel, args.order, args.wire)
     if defer:
-        traffic_key = dom_kernel + ("_pending" if pending else "_deferred")
+        traffic_key = dom_kernel + ("_pending2" if pending2 else "_pending" if pending else "_deferred")
     traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
                                traffic_key)
 
@@ -364,7 +388,8 @@ def main():
             "accumulate": "f32 fixed binary tree", "keys": "f64" if sparse else None,
             "chunk": plan.chunk or None, "keep_ratio": wl.rho if sparse else None,
             "k": plan.k if sparse else None, "n_chunks": plan.n_chunks if sparse else None,
-            "residual_mode": (("pending deferred lazy-zero" if pending else "deferred lazy-zero") if defer
+            "residual_mode": (("depth-2 pending deferred lazy-zero" if pending2 else
+                               "pending deferred lazy-zero" if pending else "deferred lazy-zero") if defer
                               else "lazy-zero") if sparse else None,
             "gradient_batches": nb,
             "fusion": "zero-copy read of %d per-layer tensors" % (W * len(wl.numels)) if layers_src

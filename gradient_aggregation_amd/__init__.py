@@ -107,6 +107,13 @@ def lib() -> ctypes.CDLL:
                                                              _VP, _VP, _VP]
         L.ga_residual_flush_layers.restype = st
         L.ga_residual_flush_layers.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_chunk_norm_layers_pending2.restype = st
+        L.ga_chunk_norm_layers_pending2.argtypes = [_VP] * 10
+        L.ga_sparse_gather_reduce_layers_pending2.restype = st
+        L.ga_sparse_gather_reduce_layers_pending2.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                              ctypes.POINTER(SGD), _VP, _VP, _VP]
+        L.ga_residual_flush_layers2.restype = st
+        L.ga_residual_flush_layers2.argtypes = [_VP] * 8
         L.ga_bucket_boundaries.restype = st
         L.ga_bucket_boundaries.argtypes = [ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP]
         L.ga_buckets_create.restype = st
@@ -375,6 +382,51 @@ class Plan:
             _dev(resid, torch.float32, self.W * self.ld, "resid"),
             _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
+
+    def chunk_norm_layers_pending2(self, layer_ptrs, prev_layer_ptrs, prev2_layer_ptrs, resid, keys, prev_mask,
+                                   prev2_mask, prev3_mask) -> None:
+        """Depth-2 pending chunk norms (masks of the previous three steps,
+        gradient tensors of the previous two)."""
+        torch = _torch()
+        n = self.W * len(self.layer_numels)
+        mwn = self.W * self.mask_words
+        _check(lib().ga_chunk_norm_layers_pending2(
+            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
+            _dev(prev_layer_ptrs, torch.int64, n, "prev_layer_ptrs"),
+            _dev(prev2_layer_ptrs, torch.int64, n, "prev2_layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, mwn, "prev_mask"), _dev(prev2_mask, torch.int32, mwn, "prev2_mask"),
+            _dev(prev3_mask, torch.int32, mwn, "prev3_mask"),
+            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
+
+    def sparse_gather_reduce_layers_pending2(self, layer_ptrs, prev_layer_ptrs, resid, prev_mask, sel_mask,
+                                             prev2_mask, grad=None, w=None, v=None, lr: Optional[float] = None,
+                                             mu: Optional[float] = None) -> None:
+        """Depth-2 pending gather-reduce."""
+        torch = _torch()
+        n = self.W * len(self.layer_numels)
+        mwn = self.W * self.mask_words
+        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
+        _check(lib().ga_sparse_gather_reduce_layers_pending2(
+            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
+            _dev(prev_layer_ptrs, torch.int64, n, "prev_layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, mwn, "prev_mask"), _dev(sel_mask, torch.int32, mwn, "sel_mask"),
+            _dev(prev2_mask, torch.int32, mwn, "prev2_mask"),
+            _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
+            _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
+
+    def residual_flush_layers2(self, layer_ptrs, prev_layer_ptrs, resid, prev_mask, sel_mask, prev2_mask) -> None:
+        """Write the pending residuals of a depth-2 step."""
+        torch = _torch()
+        n = self.W * len(self.layer_numels)
+        mwn = self.W * self.mask_words
+        _check(lib().ga_residual_flush_layers2(
+            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
+            _dev(prev_layer_ptrs, torch.int64, n, "prev_layer_ptrs"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, mwn, "prev_mask"), _dev(sel_mask, torch.int32, mwn, "sel_mask"),
+            _dev(prev2_mask, torch.int32, mwn, "prev2_mask"), _stream_ptr()))
 
     def chunk_norm(self, bucket, resid, keys, prev_mask=None) -> None:
         torch = _torch()

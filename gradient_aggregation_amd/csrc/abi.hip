@@ -367,6 +367,73 @@ ga_status ga_residual_flush_layers(const ga_plan* plan, const uint64_t* d_layer_
                          "residual_flush_layers launch");
 }
 
+ga_status ga_chunk_norm_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                        const uint64_t* d_prev_layer_ptrs, const uint64_t* d_prev2_layer_ptrs,
+                                        float* d_residual, const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask,
+                                        const uint32_t* d_prev3_mask, double* d_keys, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_prev2_layer_ptrs || !d_residual || !d_prev_mask ||
+        !d_prev2_mask || !d_prev3_mask || !d_keys)
+        return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) ||
+        ((uintptr_t)d_prev2_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_keys & 7u) ||
+        ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u) || ((uintptr_t)d_prev3_mask & 3u))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_chunk_norm_layers_pending2(*p, d_layer_ptrs, d_prev_layer_ptrs,
+                                                               d_prev2_layer_ptrs, d_residual, d_prev_mask,
+                                                               d_prev2_mask, d_prev3_mask, d_keys, stream),
+                         "chunk_norm_layers_pending2 launch");
+}
+
+ga_status ga_sparse_gather_reduce_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                                  const uint64_t* d_prev_layer_ptrs, float* d_residual,
+                                                  const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
+                                                  const uint32_t* d_prev2_mask, float* d_grad, const ga_sgd* sgd,
+                                                  float* d_w, float* d_v, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask ||
+        !d_prev2_mask)
+        return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (p->C % 256 != 0) return fail(GA_ERR_UNSUPPORTED, "chunk=%lld is not a multiple of 256", (long long)p->C);
+    if (d_prev_mask == d_sel_mask || d_prev2_mask == d_sel_mask)
+        return fail(GA_ERR_INVALID, "an earlier mask and the current mask are the same buffer");
+    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
+    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
+    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) || !aligned16(d_residual) ||
+        ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_sel_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u) ||
+        (d_grad && !aligned16(d_grad)) || (sgd && (!aligned16(d_w) || !aligned16(d_v))))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_sparse_gather_pending2(*p, d_layer_ptrs, d_prev_layer_ptrs, d_residual,
+                                                           d_prev_mask, d_sel_mask, d_prev2_mask, d_grad, sgd, d_w,
+                                                           d_v, stream),
+                         "sparse_gather_reduce_layers_pending2 launch");
+}
+
+ga_status ga_residual_flush_layers2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                    const uint64_t* d_prev_layer_ptrs, float* d_residual,
+                                    const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
+                                    const uint32_t* d_prev2_mask, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask ||
+        !d_prev2_mask)
+        return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) || !aligned16(d_residual) ||
+        ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_sel_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_residual_flush(*p, d_layer_ptrs, d_residual, d_prev_mask, d_sel_mask, stream,
+                                                   d_prev_layer_ptrs, d_prev2_mask),
+                         "residual_flush_layers2 launch");
+}
+
 ga_status ga_reduce_variant(const ga_plan* plan, const void* d_bucket, ga_order order, int32_t wire_fp16, float* d_grad,
                             const ga_sgd* sgd, float* d_w, float* d_v, hipStream_t stream) {
     if (!plan || !d_bucket) return fail(GA_ERR_INVALID, "NULL argument");

@@ -58,6 +58,27 @@ __device__ __noinline__ float4 grad4_slow(const uint64_t* __restrict__ layer_ptr
     return make_float4(f[0] + 0.f, f[1] + 0.f, f[2] + 0.f, f[3] + 0.f);
 }
 
+// Worker wk's 4 binary16 gradient elements at i0 as raw bits, two to a word
+// (zero past P), element by element, for the same cases as grad4_slow.
+__device__ __noinline__ v2u grad4_slow_raw16(const uint64_t* __restrict__ layer_ptrs,
+                                             const int64_t* __restrict__ offsets, int32_t L, int32_t wk, int32_t la,
+                                             int64_t ea, int64_t i0, int64_t P) {
+    uint32_t h[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + e;
+        if (i < P) {
+            int32_t l = la;
+            if (i >= ea) {
+                l = la + 1;
+                while (offsets[l + 1] <= i) ++l;
+            }
+            h[e] = as_global<uint16_t>(layer_ptrs[(int64_t)wk * L + l])[i - offsets[l]];
+        }
+    }
+    return v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
 // A leaf as loaded: 4 binary32 residual values; or 4 gradient elements
 // (binary16 in the first two words, or binary32) to widen and add +0 to (the
 // residual of a chunk sent in the previous step is +0, and a = leaf + residual
@@ -103,28 +124,38 @@ __device__ __forceinline__ uint64_t pick(int gi, uint64_t a0, uint64_t a1, uint6
 }
 
 // The bitmaps of the 64-worker group starting at g0 for chunk bit cb of mask
-// word cw: sent now (mc) and sent in the previous step (mp).
+// word cw: sent now (mc), sent in the previous step (mp) and, with P2, sent
+// two steps back (mq; else 0).
+template <bool P2>
 __device__ __forceinline__ void group_masks(const uint32_t* __restrict__ sel_mask,
-                                            const uint32_t* __restrict__ prev_mask, int32_t W, int32_t mw,
+                                            const uint32_t* __restrict__ prev_mask,
+                                            const uint32_t* __restrict__ prev2_mask, int32_t W, int32_t mw,
                                             int32_t cw, uint32_t cb, int32_t g0, int lane, uint64_t& mc,
-                                            uint64_t& mp) {
+                                            uint64_t& mp, uint64_t& mq) {
     const int32_t wk = g0 + lane;
     const uint32_t sc = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
     const uint32_t sp = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
+    const uint32_t sq = P2 && wk < W ? prev2_mask[(int64_t)wk * mw + cw] : 0u;
     mc = __ballot((sc & cb) != 0u);
     mp = __ballot((sp & cb) != 0u);
+    mq = P2 ? __ballot((sq & cb) != 0u) : 0ull;
 }
 
-template <int LEV, bool FP16>
+// P2 (the depth-2 pending form): a chunk sent now and two steps back but not
+// in the previous step (its a was not stored) has the leaf g0 + (g1 + 0),
+// read from this step's tensors and the previous step's (prev_layer_ptrs).
+template <int LEV, bool FP16, bool P2 = false>
 __global__ __launch_bounds__(kThreads) void k_gather_defer(
     const uint64_t* __restrict__ layer_ptrs, const int64_t* __restrict__ offsets,
     const uint32_t* __restrict__ tile_layer, int64_t tile_elems, int32_t L, float* __restrict__ resid,
     int64_t ld, int32_t W, int64_t P, int64_t C, const uint32_t* __restrict__ prev_mask,
     const uint32_t* __restrict__ sel_mask, int32_t mw, float invW, float* __restrict__ grad, int32_t do_sgd,
-    float lr, float mu, float* __restrict__ w, float* __restrict__ v) {
+    float lr, float mu, float* __restrict__ w, float* __restrict__ v,
+    const uint64_t* __restrict__ prev_layer_ptrs, const uint32_t* __restrict__ prev2_mask) {
     // W < 256 (LEV <= 8): the (at most four) groups' bitmaps and addresses
     // are read once and kept in registers; otherwise group by group.
     constexpr bool kCached = LEV <= 8;
+    constexpr int UNR = kUnroll;   // leaves in flight
     constexpr int E = 4;
     constexpr int64_t kEsz = FP16 ? 2 : 4;
     constexpr uint64_t kAlignMask = FP16 ? 7ull : 15ull;
@@ -151,14 +182,16 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     // Both bitmaps of the (at most four) 64-worker groups, every mask word in
     // flight together: sent now (mc), sent in the previous step (mp).
     uint64_t mc0 = 0ull, mc1 = 0ull, mc2 = 0ull, mc3 = 0ull, mp0 = 0ull, mp1 = 0ull, mp2 = 0ull, mp3 = 0ull;
-    bool any_sent = false, any_resent = false;
+    uint64_t mq0 = 0ull, mq1 = 0ull, mq2 = 0ull, mq3 = 0ull;
+    bool any_sent = false, any_resent = false, any_pend = false;
     if (kCached) {
-        uint32_t sw[4], pw[4];
+        uint32_t sw[4], pw[4], qw[4];
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const int32_t wk = gi * 64 + lane;
             sw[gi] = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
             pw[gi] = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
+            qw[gi] = P2 && wk < W ? prev2_mask[(int64_t)wk * mw + cw] : 0u;
         }
         mc0 = __ballot((sw[0] & cb) != 0u);
         mc1 = __ballot((sw[1] & cb) != 0u);
@@ -172,12 +205,21 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
         // some worker sent the chunk now and in the previous step: its leaf is
         // read from the gradient tensor
         any_resent = ((mc0 & mp0) | (mc1 & mp1) | (mc2 & mp2) | (mc3 & mp3)) != 0ull;
+        if (P2) {
+            // pending (sent two steps back, not in the previous step) and sent now
+            mq0 = __ballot((qw[0] & cb) != 0u) & mc0 & ~mp0;
+            mq1 = __ballot((qw[1] & cb) != 0u) & mc1 & ~mp1;
+            mq2 = __ballot((qw[2] & cb) != 0u) & mc2 & ~mp2;
+            mq3 = __ballot((qw[3] & cb) != 0u) & mc3 & ~mp3;
+            any_pend = (mq0 | mq1 | mq2 | mq3) != 0ull;
+        }
     } else {
         for (int32_t g0 = 0; g0 < W; g0 += 64) {
-            uint64_t mc, mp;
-            group_masks(sel_mask, prev_mask, W, mw, cw, cb, g0, lane, mc, mp);
+            uint64_t mc, mp, mq;
+            group_masks<P2>(sel_mask, prev_mask, prev2_mask, W, mw, cw, cb, g0, lane, mc, mp, mq);
             any_sent |= mc != 0ull;
             any_resent |= (mc & mp) != 0ull;
+            any_pend |= (mq & mc & ~mp) != 0ull;
         }
     }
 
@@ -195,7 +237,10 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     int64_t ea = end0;
     uint64_t p0 = 0ull, p1 = 0ull, p2 = 0ull, p3 = 0ull;
     bool v0 = false, v1 = false, v2 = false, v3 = false;
-    if (any_resent) {
+    // and the previous step's tensor addresses (q, vq) for the pending leaves
+    uint64_t q0 = 0ull, q1 = 0ull, q2 = 0ull, q3 = 0ull;
+    bool vq0 = false, vq1 = false, vq2 = false, vq3 = false;
+    if (any_resent || any_pend) {
         if (whole && kCached) {
             p0 = lane < W ? layer_ptrs[(int64_t)lane * L + l0] : 0ull;
             p1 = 64 + lane < W ? layer_ptrs[(int64_t)(64 + lane) * L + l0] : 0ull;
@@ -205,6 +250,16 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
             v1 = __ballot((p1 & kAlignMask) != 0ull) == 0ull;
             v2 = __ballot((p2 & kAlignMask) != 0ull) == 0ull;
             v3 = __ballot((p3 & kAlignMask) != 0ull) == 0ull;
+            if (P2 && any_pend) {
+                q0 = lane < W ? prev_layer_ptrs[(int64_t)lane * L + l0] : 0ull;
+                q1 = 64 + lane < W ? prev_layer_ptrs[(int64_t)(64 + lane) * L + l0] : 0ull;
+                q2 = 128 + lane < W ? prev_layer_ptrs[(int64_t)(128 + lane) * L + l0] : 0ull;
+                q3 = 192 + lane < W ? prev_layer_ptrs[(int64_t)(192 + lane) * L + l0] : 0ull;
+                vq0 = __ballot((q0 & kAlignMask) != 0ull) == 0ull;
+                vq1 = __ballot((q1 & kAlignMask) != 0ull) == 0ull;
+                vq2 = __ballot((q2 & kAlignMask) != 0ull) == 0ull;
+                vq3 = __ballot((q3 & kAlignMask) != 0ull) == 0ull;
+            }
         } else if (!whole && valid) {
             int32_t lo = l0, hi = L;   // the lane's layer is l0 or a later one
             while (lo < hi) {
@@ -224,44 +279,81 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
         uint32_t cnt = 0;
         for (int32_t g0 = 0; g0 < W; g0 += 64) {
             const int gi = g0 >> 6;
-            uint64_t mc, mp, mine;
-            bool vec;
+            uint64_t mc, mp, mq, mine, prv;
+            bool vec, vecq;
             if (kCached) {
                 mc = pick(gi, mc0, mc1, mc2, mc3);
                 mp = pick(gi, mp0, mp1, mp2, mp3);
+                mq = pick(gi, mq0, mq1, mq2, mq3);
                 mine = pick(gi, p0, p1, p2, p3);
+                prv = pick(gi, q0, q1, q2, q3);
                 vec = gi == 0 ? v0 : gi == 1 ? v1 : gi == 2 ? v2 : v3;
+                vecq = gi == 0 ? vq0 : gi == 1 ? vq1 : gi == 2 ? vq2 : vq3;
             } else {
-                group_masks(sel_mask, prev_mask, W, mw, cw, cb, g0, lane, mc, mp);
-                mine = 0ull;
-                vec = false;
-                if (whole && (mc & mp) != 0ull) {
+                group_masks<P2>(sel_mask, prev_mask, prev2_mask, W, mw, cw, cb, g0, lane, mc, mp, mq);
+                mq &= mc & ~mp;
+                mine = prv = 0ull;
+                vec = vecq = false;
+                if (whole && ((mc & mp) | mq) != 0ull) {
                     mine = g0 + lane < W ? layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
                     vec = __ballot((mine & kAlignMask) != 0ull) == 0ull;
                 }
+                if (P2 && whole && mq != 0ull) {
+                    prv = g0 + lane < W ? prev_layer_ptrs[(int64_t)(g0 + lane) * L + l0] : 0ull;
+                    vecq = __ballot((prv & kAlignMask) != 0ull) == 0ull;
+                }
             }
             const int32_t gn = W - g0 < 64 ? W - g0 : 64;
-            for (int32_t u0 = 0; u0 < gn; u0 += kUnroll) {
-                v4u x[kUnroll];
+            for (int32_t u0 = 0; u0 < gn; u0 += UNR) {
+                // y: the previous step's gradient of a pending leaf (binary16:
+                // 4 elements as raw bits in two words; binary32: 4 words)
+                v4u x[UNR];
+                v2u y2[P2 ? UNR : 1];
+                v4u y4[P2 && !FP16 ? UNR : 1];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < UNR; ++u) {
                     x[u] = v4u{0u, 0u, 0u, 0u};
+                    if (P2) {
+                        y2[u] = v2u{0u, 0u};
+                        if (!FP16) y4[u] = v4u{0u, 0u, 0u, 0u};
+                    }
                     const int32_t b = u0 + u;
                     if (b < gn && ((mc >> b) & 1ull) && valid) {
-                        if ((mp >> b) & 1ull)
+                        if (((mp >> b) & 1ull) || (P2 && ((mq >> b) & 1ull)))
                             x[u] = load_grad<FP16>(vec, mine, b, byte_off, layer_ptrs, offsets, L, g0 + b, la, ea,
                                                    i0, P);
                         else
                             x[u] = __builtin_nontemporal_load(
                                 reinterpret_cast<const v4u*>(resid + (int64_t)(g0 + b) * ld + i0));
+                        if (P2 && ((mq >> b) & 1ull)) {
+                            if (FP16 && !vecq) {
+                                y2[u] = grad4_slow_raw16(prev_layer_ptrs, offsets, L, g0 + b, la, ea, i0, P);
+                            } else {
+                                const v4u t = load_grad<FP16>(vecq, prv, b, byte_off, prev_layer_ptrs, offsets, L,
+                                                              g0 + b, la, ea, i0, P);
+                                if (FP16) y2[u] = v2u{t.x, t.y};
+                                else y4[u] = t;
+                            }
+                        }
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < UNR; ++u) {
                     const int32_t b = u0 + u;
                     if (b < gn) {
-                        const int kind = (((mc & mp) >> b) & 1ull) ? (vec ? kGradVec : kReady) : kResid;
-                        const float4 a = decode_leaf<FP16>(x[u], kind);
+                        const bool pend = P2 && ((mq >> b) & 1ull);
+                        const int kind =
+                            ((((mc & mp) >> b) & 1ull) || pend) ? (vec ? kGradVec : kReady) : kResid;
+                        float4 a = decode_leaf<FP16>(x[u], kind);
+                        if (P2 && pend) {
+                            // a = g0 + (g1 + 0): adding +0 to g0 as well changes
+                            // nothing, since g1 + 0 is never -0
+                            // binary16: raw bits on both load paths
+                            const float4 r1 =
+                                FP16 ? decode_leaf<FP16>(v4u{y2[u].x, y2[u].y, 0u, 0u}, kGradVec)
+                                     : decode_leaf<FP16>(y4[FP16 ? 0 : u], vecq ? kGradVec : kReady);
+                            a.x += r1.x; a.y += r1.y; a.z += r1.z; a.w += r1.w;
+                        }
                         float f[E] = {a.x, a.y, a.z, a.w};
                         tree.push(f, cnt);
                         ++cnt;
@@ -345,31 +437,74 @@ __device__ __forceinline__ void copy_segment(gptr<void> __restrict__ src, int64_
                0.f;
 }
 
+// Residual = g0 + (g1 + 0) on the elements [ss, se) of one worker, g0 from
+// this step's tensor src and g1 from the previous step's psrc, at the same
+// offsets; with vec_ok, both are 16-byte aligned at ss.
+template <bool FP16>
+__device__ __forceinline__ void copy2_segment(gptr<void> __restrict__ src, gptr<void> __restrict__ psrc,
+                                              int64_t soff, bool vec_ok, float* __restrict__ r, int64_t ss,
+                                              int64_t se) {
+    const int64_t nvec = vec_ok ? (se - ss) >> 3 : 0;
+    for (int64_t j = threadIdx.x; j < nvec; j += kThreads) {
+        const int64_t i = ss + (j << 3);
+        float f[8], q[8];
+        if (FP16) {
+            widen8(load_u4(static_cast<gptr<uint16_t>>(src) + (i - soff)), f);
+            widen8(load_u4(static_cast<gptr<uint16_t>>(psrc) + (i - soff)), q);
+        } else {
+            gptr<float> gp = static_cast<gptr<float>>(src) + (i - soff);
+            gptr<float> pp = static_cast<gptr<float>>(psrc) + (i - soff);
+            const float4 g0 = load_f4(gp), g1 = load_f4(gp + 4), p0 = load_f4(pp), p1 = load_f4(pp + 4);
+            f[0] = g0.x; f[1] = g0.y; f[2] = g0.z; f[3] = g0.w; f[4] = g1.x; f[5] = g1.y; f[6] = g1.z; f[7] = g1.w;
+            q[0] = p0.x; q[1] = p0.y; q[2] = p0.z; q[3] = p0.w; q[4] = p1.x; q[5] = p1.y; q[6] = p1.z; q[7] = p1.w;
+        }
+        *reinterpret_cast<float4*>(r + i) =
+            make_float4(f[0] + (q[0] + 0.f), f[1] + (q[1] + 0.f), f[2] + (q[2] + 0.f), f[3] + (q[3] + 0.f));
+        *reinterpret_cast<float4*>(r + i + 4) =
+            make_float4(f[4] + (q[4] + 0.f), f[5] + (q[5] + 0.f), f[6] + (q[6] + 0.f), f[7] + (q[7] + 0.f));
+    }
+    for (int64_t i = ss + (nvec << 3) + threadIdx.x; i < se; i += kThreads) {
+        const float f = FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i - soff])
+                             : static_cast<gptr<float>>(src)[i - soff];
+        const float q = FP16 ? widen1(static_cast<gptr<uint16_t>>(psrc)[i - soff])
+                             : static_cast<gptr<float>>(psrc)[i - soff];
+        r[i] = f + (q + 0.f);
+    }
+}
+
 // kMatParts workgroups per (worker, 32-chunk mask word): they write, each its
 // share of every chunk, the chunks of that word the worker sent in the
-// previous step but not now (their residual is the widened gradient).  Most
-// words have none or one such chunk, so the grid stays far smaller than one
-// workgroup per (worker, chunk).
+// previous step but not now (their residual is the widened gradient) and,
+// with P2, those sent two steps back and in neither later step (their
+// residual is g0 + (g1 + 0), from this step's and the previous step's
+// tensors).  Most words have none or one such chunk, so the grid stays far
+// smaller than one workgroup per (worker, chunk).
 constexpr int kMatParts = 4;
-template <bool FP16>
+template <bool FP16, bool P2 = false>
 __global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __restrict__ layer_ptrs,
                                                           const int64_t* __restrict__ offsets,
                                                           const uint32_t* __restrict__ tile_layer, int64_t tile_elems,
                                                           int32_t L,
                                                           float* __restrict__ resid, int64_t ld, int64_t P, int64_t C,
                                                           int32_t n_c, const uint32_t* __restrict__ prev_mask,
-                                                          const uint32_t* __restrict__ sel_mask, int32_t mw) {
+                                                          const uint32_t* __restrict__ sel_mask, int32_t mw,
+                                                          const uint64_t* __restrict__ prev_layer_ptrs,
+                                                          const uint32_t* __restrict__ prev2_mask) {
     const int64_t b = blockIdx.x / kMatParts;
     const int32_t part = (int32_t)(blockIdx.x % kMatParts);
     const int32_t w = (int32_t)(b / mw);
     const int32_t q = (int32_t)(b - (int64_t)w * mw);
     const int64_t word = (int64_t)w * mw + q;
-    uint32_t bits = prev_mask[word] & ~sel_mask[word];
+    const uint32_t bits1 = prev_mask[word] & ~sel_mask[word];
+    uint32_t bits = bits1;
+    if (P2) bits |= prev2_mask[word] & ~prev_mask[word] & ~sel_mask[word];
     float* __restrict__ r = resid + (int64_t)w * ld;
     // this workgroup's share of each chunk: a multiple of 8 elements
     const int64_t share = (C / kMatParts + 7) / 8 * 8;
     while (bits != 0u) {
-        const int32_t c = q * 32 + __builtin_ctz(bits);
+        const int32_t cbit = __builtin_ctz(bits);
+        const int32_t c = q * 32 + cbit;
+        const bool two = P2 && !((bits1 >> cbit) & 1u);
         bits &= bits - 1u;
         if (c >= n_c) break;
         const int64_t c0 = (int64_t)c * C;
@@ -385,44 +520,64 @@ __global__ __launch_bounds__(kThreads) void k_materialize(const uint64_t* __rest
             const int64_t off = offsets[l], end = offsets[l + 1];
             const uint64_t addr = layer_ptrs[(int64_t)w * L + l];
             const bool vec_ok = (off & 7) == 0 && (addr & 15) == 0;
-            copy_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e);
+            if (P2 && two) {
+                const uint64_t paddr = prev_layer_ptrs[(int64_t)w * L + l];
+                copy2_segment<FP16>(as_global<void>(addr), as_global<void>(paddr), off, vec_ok && (paddr & 15) == 0,
+                                    r, off > s ? off : s, end < e ? end : e);
+            } else {
+                copy_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e);
+            }
         }
     }
 }
 
 // k_materialize over every (worker, mask word): the residual of each chunk
-// set in prev_mask but not in sel_mask becomes the widened gradient + 0.
+// set in prev_mask but not in sel_mask becomes the widened gradient + 0; with
+// prev2_mask (the depth-2 pending form), also that of each chunk set in
+// prev2_mask and in neither later mask, g0 + (g1 + 0).
 hipError_t materialize_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resid,
-                                const uint32_t* prev_mask, const uint32_t* sel_mask, hipStream_t s) {
+                                const uint32_t* prev_mask, const uint32_t* sel_mask, hipStream_t s,
+                                const uint64_t* prev_layer_ptrs = nullptr, const uint32_t* prev2_mask = nullptr) {
     const int64_t words = (int64_t)p.W * p.mw * kMatParts;
     if (words == 0) return hipSuccess;
-    if (p.dtype == GA_FP16)
-        hipLaunchKernelGGL((k_materialize<true>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
-                           prev_mask, sel_mask, p.mw);
-    else
-        hipLaunchKernelGGL((k_materialize<false>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c,
-                           prev_mask, sel_mask, p.mw);
+#define GA_MAT_LAUNCH(F, Q)                                                                                    \
+    hipLaunchKernelGGL((k_materialize<F, Q>), dim3((unsigned)words), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets, \
+                       p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.P, p.C, (int32_t)p.n_c, prev_mask,    \
+                       sel_mask, p.mw, prev_layer_ptrs, prev2_mask)
+    const bool two = prev2_mask != nullptr;
+    if (p.dtype == GA_FP16) {
+        if (two) GA_MAT_LAUNCH(true, true);
+        else GA_MAT_LAUNCH(true, false);
+    } else {
+        if (two) GA_MAT_LAUNCH(false, true);
+        else GA_MAT_LAUNCH(false, false);
+    }
+#undef GA_MAT_LAUNCH
     return hipGetLastError();
 }
 
 template <int LEV>
 hipError_t defer_dispatch(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
                           const uint32_t* sel_mask, float* grad, const ga_sgd* sgd, float* w, float* v,
-                          bool materialize, hipStream_t s) {
+                          bool materialize, hipStream_t s, const uint64_t* prev_layer_ptrs = nullptr,
+                          const uint32_t* prev2_mask = nullptr) {
     const int64_t threads = (p.P + 3) / 4;
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
     const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
-    if (p.dtype == GA_FP16)
-        hipLaunchKernelGGL((k_gather_defer<LEV, true>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets,
-                           p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask, sel_mask, p.mw,
-                           invW, grad, sgd ? 1 : 0, lr, mu, w, v);
-    else
-        hipLaunchKernelGGL((k_gather_defer<LEV, false>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs,
-                           p.d_offsets, p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask,
-                           sel_mask, p.mw, invW, grad, sgd ? 1 : 0, lr, mu, w, v);
+#define GA_GATHER_LAUNCH(F, Q)                                                                                 \
+    hipLaunchKernelGGL((k_gather_defer<LEV, F, Q>), dim3(blocks), dim3(kThreads), 0, s, layer_ptrs, p.d_offsets, \
+                       p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, prev_mask, sel_mask, p.mw, \
+                       invW, grad, sgd ? 1 : 0, lr, mu, w, v, prev_layer_ptrs, prev2_mask)
+    const bool two = prev2_mask != nullptr;
+    if (p.dtype == GA_FP16) {
+        if (two) GA_GATHER_LAUNCH(true, true);
+        else GA_GATHER_LAUNCH(true, false);
+    } else {
+        if (two) GA_GATHER_LAUNCH(false, true);
+        else GA_GATHER_LAUNCH(false, false);
+    }
+#undef GA_GATHER_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !materialize) return e;
     // the (worker, chunk) pairs written here are disjoint from those the
@@ -443,10 +598,26 @@ hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs,
     return defer_dispatch<11>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, materialize, s);
 }
 
-hipError_t launch_residual_flush(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
-                                 const uint32_t* sel_mask, hipStream_t s) {
+hipError_t launch_sparse_gather_pending2(const Plan& p, const uint64_t* layer_ptrs, const uint64_t* prev_layer_ptrs,
+                                         float* resid, const uint32_t* prev_mask, const uint32_t* sel_mask,
+                                         const uint32_t* prev2_mask, float* grad, const ga_sgd* sgd, float* w,
+                                         float* v, hipStream_t s) {
     if (p.P == 0) return hipSuccess;
-    return materialize_dispatch(p, layer_ptrs, resid, prev_mask, sel_mask, s);
+    if (p.W < (1 << 5))
+        return defer_dispatch<5>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, false, s,
+                                 prev_layer_ptrs, prev2_mask);
+    if (p.W < (1 << 8))
+        return defer_dispatch<8>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, false, s,
+                                 prev_layer_ptrs, prev2_mask);
+    return defer_dispatch<11>(p, layer_ptrs, resid, prev_mask, sel_mask, grad, sgd, w, v, false, s,
+                              prev_layer_ptrs, prev2_mask);
+}
+
+hipError_t launch_residual_flush(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
+                                 const uint32_t* sel_mask, hipStream_t s, const uint64_t* prev_layer_ptrs,
+                                 const uint32_t* prev2_mask) {
+    if (p.P == 0) return hipSuccess;
+    return materialize_dispatch(p, layer_ptrs, resid, prev_mask, sel_mask, s, prev_layer_ptrs, prev2_mask);
 }
 
 }  // namespace ga

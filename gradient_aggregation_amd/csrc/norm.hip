@@ -14,7 +14,10 @@
 // previous step is taken as zero and not read.  In the pending form the residual of a
 // chunk sent two steps ago but not in the previous step is still held as the
 // previous step's gradient (it was that gradient plus +0) and is read from
-// those tensors: 2 B per binary16 element instead of 4.
+// those tensors: 2 B per binary16 element instead of 4.  In the depth-2
+// pending form such a chunk does not store its a either (the later passes
+// recompute it from the two gradients), and a chunk sent three steps ago and
+// not since reads its residual from the previous two steps' gradients.
 #include "device.h"
 #include "plan.h"
 
@@ -33,6 +36,25 @@ __device__ __forceinline__ double wave_sum(double x) {
 // ---------------------------------------------------------------------------
 // k_chunk_norm
 // ---------------------------------------------------------------------------
+
+// Gradient elements j .. j+7 (one 16-byte aligned vector), or element j, of
+// the tensor src, widened to binary32.
+template <bool FP16>
+__device__ __forceinline__ void load8(gptr<void> src, int64_t j, float (&f)[8]) {
+    if (FP16) {
+        widen8(load_u4(static_cast<gptr<uint16_t>>(src) + j), f);
+    } else {
+        gptr<float> gp = static_cast<gptr<float>>(src) + j;
+        const float4 g0 = load_f4(gp), g1 = load_f4(gp + 4);
+        f[0] = g0.x; f[1] = g0.y; f[2] = g0.z; f[3] = g0.w;
+        f[4] = g1.x; f[5] = g1.y; f[6] = g1.z; f[7] = g1.w;
+    }
+}
+
+template <bool FP16>
+__device__ __forceinline__ float load1(gptr<void> src, int64_t j) {
+    return FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[j]) : static_cast<gptr<float>>(src)[j];
+}
 
 // Flat elements [ss, se) of one worker: gradient element i is src[i - soff]
 // (src typed by FP16), residual element i is r[i].  With vec_ok, ss is a
@@ -116,37 +138,33 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
     }
 }
 
-// Flat elements [ss, se) of one worker whose residual is pending: it is the
-// previous step's gradient plus +0 (a chunk sent two steps ago, so its
-// residual was zero, and not sent in the previous step), read from that
-// step's tensor psrc at the same offsets as the gradient src.  a = leaf +
-// residual is stored.  With vec_ok, both tensors are 16-byte aligned at ss.
-template <bool FP16>
-__device__ __forceinline__ void norm_segment_pending(gptr<void> __restrict__ src, gptr<void> __restrict__ psrc,
-                                                     int64_t soff, bool vec_ok, float* __restrict__ r, int64_t ss,
-                                                     int64_t se, double& acc0, double& acc1) {
-    constexpr int UN = 4;
+// Flat elements [ss, se) of one worker whose residual is pending, that is,
+// still held as the gradients of the steps since the chunk was last sent
+// (its residual was zero then): with NP = 1 the previous step's gradient p1
+// (residual = p1 + 0), with NP = 2 the previous two, p1 the later
+// (residual = p1 + (p2 + 0)), read at the same offsets as the gradient src.
+// a = leaf + residual is stored if STORE.  With vec_ok, all the tensors are
+// 16-byte aligned at ss.
+template <bool FP16, int NP, bool STORE>
+__device__ __forceinline__ void norm_segment_pending(gptr<void> __restrict__ src, gptr<void> __restrict__ p1,
+                                                     gptr<void> __restrict__ p2, int64_t soff, bool vec_ok,
+                                                     float* __restrict__ r, int64_t ss, int64_t se, double& acc0,
+                                                     double& acc1) {
+    constexpr int UN = NP == 1 ? 4 : 2;
     const int64_t nvec = vec_ok ? (se - ss) >> 3 : 0;
     int64_t j = threadIdx.x;
     for (; j < nvec; j += UN * kNormThreads) {
-        float lf[UN][8], pf[UN][8];
+        float lf[UN][8], rv[UN][8];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
-            const int64_t i = ss + ((j + u * kNormThreads) << 3);
             if (j + u * kNormThreads >= nvec) continue;
-            if (FP16) {
-                widen8(load_u4(static_cast<gptr<uint16_t>>(src) + (i - soff)), lf[u]);
-                widen8(load_u4(static_cast<gptr<uint16_t>>(psrc) + (i - soff)), pf[u]);
-            } else {
-                gptr<float> gp = static_cast<gptr<float>>(src) + (i - soff);
-                gptr<float> pp = static_cast<gptr<float>>(psrc) + (i - soff);
-                const float4 g0 = load_f4(gp), g1 = load_f4(gp + 4);
-                const float4 p0 = load_f4(pp), p1 = load_f4(pp + 4);
-                lf[u][0] = g0.x; lf[u][1] = g0.y; lf[u][2] = g0.z; lf[u][3] = g0.w;
-                lf[u][4] = g1.x; lf[u][5] = g1.y; lf[u][6] = g1.z; lf[u][7] = g1.w;
-                pf[u][0] = p0.x; pf[u][1] = p0.y; pf[u][2] = p0.z; pf[u][3] = p0.w;
-                pf[u][4] = p1.x; pf[u][5] = p1.y; pf[u][6] = p1.z; pf[u][7] = p1.w;
-            }
+            const int64_t i = ss + ((j + u * kNormThreads) << 3);
+            float q1[8], q2[8];
+            load8<FP16>(src, i - soff, lf[u]);
+            load8<FP16>(p1, i - soff, q1);
+            if (NP == 2) load8<FP16>(p2, i - soff, q2);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) rv[u][q] = NP == 2 ? q1[q] + (q2[q] + 0.f) : q1[q] + 0.f;
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
@@ -155,21 +173,22 @@ __device__ __forceinline__ void norm_segment_pending(gptr<void> __restrict__ src
             float a[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                a[q] = lf[u][q] + (pf[u][q] + 0.f);
+                a[q] = lf[u][q] + rv[u][q];
                 if (q & 1) acc1 = fma((double)a[q], (double)a[q], acc1);
                 else acc0 = fma((double)a[q], (double)a[q], acc0);
             }
-            *reinterpret_cast<float4*>(r + i) = make_float4(a[0], a[1], a[2], a[3]);
-            *reinterpret_cast<float4*>(r + i + 4) = make_float4(a[4], a[5], a[6], a[7]);
+            if (STORE) {
+                *reinterpret_cast<float4*>(r + i) = make_float4(a[0], a[1], a[2], a[3]);
+                *reinterpret_cast<float4*>(r + i + 4) = make_float4(a[4], a[5], a[6], a[7]);
+            }
         }
     }
     for (int64_t i = ss + (nvec << 3) + threadIdx.x; i < se; i += kNormThreads) {
-        const float lf = FP16 ? widen1(static_cast<gptr<uint16_t>>(src)[i - soff])
-                              : static_cast<gptr<float>>(src)[i - soff];
-        const float pf = FP16 ? widen1(static_cast<gptr<uint16_t>>(psrc)[i - soff])
-                              : static_cast<gptr<float>>(psrc)[i - soff];
-        const float a = lf + (pf + 0.f);
-        r[i] = a;
+        const float lf = load1<FP16>(src, i - soff);
+        const float q1 = load1<FP16>(p1, i - soff);
+        const float rv = NP == 2 ? q1 + (load1<FP16>(p2, i - soff) + 0.f) : q1 + 0.f;
+        const float a = lf + rv;
+        if (STORE) r[i] = a;
         acc0 = fma((double)a, (double)a, acc0);
     }
 }
@@ -182,15 +201,21 @@ __device__ __forceinline__ void norm_segment_pending(gptr<void> __restrict__ src
 // computes its key but does not store a, which is the widened gradient; the
 // deferred gather reads the gradient for it instead, and writes it as the
 // residual if the chunk is not sent again.
-// PEND (with DEFER): a chunk set in prev2_mask (sent two steps ago) but not
-// in prev_mask has the previous step's gradient as its residual, read from
-// prev_layer_ptrs (the previous step's layer table) instead of resid.
-template <bool FP16, bool LAZY, bool LAYERS, bool DEFER = false, bool PEND = false>
+// DEPTH >= 1 (with DEFER, the pending forms): a chunk set in prev2_mask
+// (sent two steps ago) but not in prev_mask has the previous step's gradient
+// + 0 as its residual, read from prev_layer_ptrs (the previous step's layer
+// table) instead of resid; with DEPTH 1 its a is stored, with DEPTH 2 it is
+// not.  DEPTH 2: a chunk set in prev3_mask (sent three steps ago) and in
+// neither prev2_mask nor prev_mask has the residual g1 + (g2 + 0), g1 and g2
+// read from prev_layer_ptrs and prev2_layer_ptrs (two steps back); its a is
+// stored.
+template <bool FP16, bool LAZY, bool LAYERS, bool DEFER = false, int DEPTH = 0>
 __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     const void* __restrict__ bucket, const uint64_t* __restrict__ layer_ptrs,
     const int64_t* __restrict__ offsets, int32_t L, float* __restrict__ resid, int64_t ld, int64_t P,
     int64_t C, int32_t n_c, const uint32_t* __restrict__ prev_mask, int32_t mw, double* __restrict__ keys,
-    const uint64_t* __restrict__ prev_layer_ptrs, const uint32_t* __restrict__ prev2_mask) {
+    const uint64_t* __restrict__ prev_layer_ptrs, const uint32_t* __restrict__ prev2_mask,
+    const uint64_t* __restrict__ prev2_layer_ptrs, const uint32_t* __restrict__ prev3_mask) {
     const int32_t w = (int32_t)blockIdx.y;
     const int32_t c = (int32_t)blockIdx.x;
     const int64_t b = (int64_t)w * n_c + c;
@@ -198,8 +223,9 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     const int64_t e = s + C < P ? s + C : P;
     bool rzero = false;
     if (LAZY) rzero = (prev_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
-    bool pend = false;
-    if (PEND && !rzero) pend = (prev2_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
+    bool pend = false, pend2 = false;
+    if (DEPTH >= 1 && !rzero) pend = (prev2_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
+    if (DEPTH >= 2 && !rzero && !pend) pend2 = (prev3_mask[(int64_t)w * mw + (c >> 5)] >> (c & 31)) & 1u;
 
     float* __restrict__ r = resid + (int64_t)w * ld;
     double acc0 = 0.0, acc1 = 0.0;
@@ -218,11 +244,18 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
             if (DEFER && rzero) {
                 norm_segment<FP16, false>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s,
                                           end < e ? end : e, rzero, acc0, acc1);
-            } else if (PEND && pend) {
-                const uint64_t paddr = prev_layer_ptrs[(int64_t)w * L + l];
-                norm_segment_pending<FP16>(as_global<void>(addr), as_global<void>(paddr), off,
-                                           vec_ok && (paddr & 15) == 0, r, off > s ? off : s, end < e ? end : e,
-                                           acc0, acc1);
+            } else if (DEPTH >= 1 && pend) {
+                const uint64_t a1 = prev_layer_ptrs[(int64_t)w * L + l];
+                norm_segment_pending<FP16, 1, DEPTH == 1>(as_global<void>(addr), as_global<void>(a1),
+                                                          as_global<void>(a1), off, vec_ok && (a1 & 15) == 0, r,
+                                                          off > s ? off : s, end < e ? end : e, acc0, acc1);
+            } else if (DEPTH >= 2 && pend2) {
+                const uint64_t a1 = prev_layer_ptrs[(int64_t)w * L + l];
+                const uint64_t a2 = prev2_layer_ptrs[(int64_t)w * L + l];
+                norm_segment_pending<FP16, 2, true>(as_global<void>(addr), as_global<void>(a1),
+                                                    as_global<void>(a2), off,
+                                                    vec_ok && (a1 & 15) == 0 && (a2 & 15) == 0, r,
+                                                    off > s ? off : s, end < e ? end : e, acc0, acc1);
             } else
                 norm_segment<FP16>(as_global<void>(addr), off, vec_ok, r, off > s ? off : s, end < e ? end : e,
                                    rzero, acc0, acc1);
@@ -245,20 +278,21 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(
     }
 }
 
-template <bool LAYERS, bool DEFER = false, bool PEND = false>
+template <bool LAYERS, bool DEFER = false, int DEPTH = 0>
 hipError_t norm_dispatch(const Plan& p, const void* bucket, const uint64_t* layer_ptrs, float* resid,
                          const uint32_t* prev_mask, double* keys, hipStream_t s,
-                         const uint64_t* prev_layer_ptrs = nullptr, const uint32_t* prev2_mask = nullptr) {
+                         const uint64_t* prev_layer_ptrs = nullptr, const uint32_t* prev2_mask = nullptr,
+                         const uint64_t* prev2_layer_ptrs = nullptr, const uint32_t* prev3_mask = nullptr) {
     // a 2-D grid: W * n_c workgroups would exceed the 32-bit work-item count
     // of a 1-D dispatch at the plan limits
     if (p.W == 0 || p.n_c == 0) return hipSuccess;
     const bool f16 = p.dtype == GA_FP16;
     const int32_t n_c = (int32_t)p.n_c;
 #define GA_NORM_LAUNCH(F, Z)                                                                               \
-    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z, PEND && Z>),                                \
+    hipLaunchKernelGGL((k_chunk_norm<F, Z, LAYERS, DEFER && Z, Z ? DEPTH : 0>),                           \
                        dim3((unsigned)p.n_c, (unsigned)p.W), dim3(kNormThreads), 0, s, bucket, layer_ptrs,     \
                        p.d_offsets, p.L, resid, p.ld, p.P, p.C, n_c, prev_mask, p.mw, keys, prev_layer_ptrs,  \
-                       prev2_mask)
+                       prev2_mask, prev2_layer_ptrs, prev3_mask)
     if (f16 && prev_mask) GA_NORM_LAUNCH(true, true);
     else if (f16) GA_NORM_LAUNCH(true, false);
     else if (prev_mask) GA_NORM_LAUNCH(false, true);
@@ -288,8 +322,16 @@ hipError_t launch_chunk_norm_layers_pending(const Plan& p, const uint64_t* layer
                                             const uint64_t* prev_layer_ptrs, float* resid,
                                             const uint32_t* prev_mask, const uint32_t* prev2_mask, double* keys,
                                             hipStream_t s) {
-    return norm_dispatch<true, true, true>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s, prev_layer_ptrs,
-                                           prev2_mask);
+    return norm_dispatch<true, true, 1>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s, prev_layer_ptrs,
+                                        prev2_mask);
+}
+
+hipError_t launch_chunk_norm_layers_pending2(const Plan& p, const uint64_t* layer_ptrs,
+                                             const uint64_t* prev_layer_ptrs, const uint64_t* prev2_layer_ptrs,
+                                             float* resid, const uint32_t* prev_mask, const uint32_t* prev2_mask,
+                                             const uint32_t* prev3_mask, double* keys, hipStream_t s) {
+    return norm_dispatch<true, true, 2>(p, nullptr, layer_ptrs, resid, prev_mask, keys, s, prev_layer_ptrs,
+                                        prev2_mask, prev2_layer_ptrs, prev3_mask);
 }
 
 }  // namespace ga

@@ -61,9 +61,27 @@ hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs,
                                       const uint32_t* prev_mask, const uint32_t* sel_mask, float* grad,
                                       const ga_sgd* sgd, float* w, float* v, bool materialize, hipStream_t s);
 // The residual of every chunk set in prev_mask but not in sel_mask becomes
-// the widened gradient (layer_ptrs) + 0.
+// the widened gradient (layer_ptrs) + 0; with prev2_mask (depth 2), that of
+// every chunk set in prev2_mask and in neither later mask becomes g0 + (g1 +
+// 0), g1 from prev_layer_ptrs.
 hipError_t launch_residual_flush(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
-                                 const uint32_t* sel_mask, hipStream_t s);
+                                 const uint32_t* sel_mask, hipStream_t s, const uint64_t* prev_layer_ptrs = nullptr,
+                                 const uint32_t* prev2_mask = nullptr);
+// Depth-2 pending form of the norm pass: launch_chunk_norm_layers_pending,
+// except that a chunk pending one step does not store its a, and a chunk set
+// in prev3_mask and in neither later mask takes g1 + (g2 + 0) as its
+// residual (prev_layer_ptrs, prev2_layer_ptrs).
+hipError_t launch_chunk_norm_layers_pending2(const Plan& p, const uint64_t* layer_ptrs,
+                                             const uint64_t* prev_layer_ptrs, const uint64_t* prev2_layer_ptrs,
+                                             float* resid, const uint32_t* prev_mask, const uint32_t* prev2_mask,
+                                             const uint32_t* prev3_mask, double* keys, hipStream_t s);
+// Depth-2 pending gather: as launch_sparse_gather_defer without
+// materialization, and a chunk sent now, set in prev2_mask and not in
+// prev_mask has the leaf g0 + (g1 + 0), g1 from prev_layer_ptrs.
+hipError_t launch_sparse_gather_pending2(const Plan& p, const uint64_t* layer_ptrs, const uint64_t* prev_layer_ptrs,
+                                         float* resid, const uint32_t* prev_mask, const uint32_t* sel_mask,
+                                         const uint32_t* prev2_mask, float* grad, const ga_sgd* sgd, float* w,
+                                         float* v, hipStream_t s);
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
 // launch_tree_layers over a sub-list of layers: worker w's layer l is entry

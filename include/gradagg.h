@@ -349,6 +349,59 @@ ga_status ga_residual_flush_layers(const ga_plan* plan, const uint64_t* d_layer_
                                    const uint32_t* d_prev_mask, const uint32_t* d_sel_mask, hipStream_t stream);
 
 /*
+ * Depth-2 pending form [GF]: as the pending form, and a chunk pending at step
+ * t (sent in step t-2, not in step t-1) does not store its a either: that a
+ * is g_t + (g_{t-1} + 0), recomputed from the two gradients by the gather
+ * (if the chunk is sent now), by the next norm pass (if not), or by
+ * ga_residual_flush_layers2.  The caller keeps the gradient tensors of the
+ * previous two steps, unchanged, and three mask buffers used in turn: the
+ * buffer the top-k of step t writes holds step t-3's mask, which the norm
+ * pass reads first.  One step t is
+ *   ga_chunk_norm_layers_pending2(g_t, g_{t-1}, g_{t-2}, m_{t-1}, m_{t-2}, m_{t-3}) ->
+ *   ga_chunk_topk(into m_{t-3}'s buffer: m_t) ->
+ *   ga_sparse_gather_reduce_layers_pending2(g_t, g_{t-1}, m_{t-1}, m_t, m_{t-2})
+ * with all-zero masks (and any valid layer tables) for the steps before the
+ * first.  Keys, selection, mean gradient, w and v are those of the lazy-zero
+ * sequence, bit for bit.
+ *
+ * ga_chunk_norm_layers_pending2: as ga_chunk_norm_layers_pending with
+ *   d_prev_mask = m_{t-1}, d_prev2_mask = m_{t-2}, except that the a of a
+ *   chunk set in d_prev2_mask but not in d_prev_mask is not stored; and a
+ *   chunk set in d_prev3_mask (m_{t-3}) and in neither later mask takes
+ *   g_{t-1} + (g_{t-2} + 0) as its residual (d_residual is not read there;
+ *   d_prev2_layer_ptrs: the tensors of step t-2); its a is stored.
+ */
+ga_status ga_chunk_norm_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                        const uint64_t* d_prev_layer_ptrs, const uint64_t* d_prev2_layer_ptrs,
+                                        float* d_residual, const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask,
+                                        const uint32_t* d_prev3_mask, double* d_keys, hipStream_t stream);
+
+/*
+ * ga_sparse_gather_reduce_layers_pending2: ga_sparse_gather_reduce_layers_pending,
+ * and the leaf of a chunk sent now (d_sel_mask), set in d_prev2_mask and not
+ * in d_prev_mask is g_t + (g_{t-1} + 0), read from d_layer_ptrs and
+ * d_prev_layer_ptrs.  d_sel_mask must differ from both earlier masks
+ * (GA_ERR_INVALID); otherwise as ga_sparse_gather_reduce_layers_pending.
+ */
+ga_status ga_sparse_gather_reduce_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                                  const uint64_t* d_prev_layer_ptrs, float* d_residual,
+                                                  const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
+                                                  const uint32_t* d_prev2_mask, float* d_grad, const ga_sgd* sgd,
+                                                  float* d_w, float* d_v, hipStream_t stream);
+
+/*
+ * ga_residual_flush_layers2: writes the pending residuals of a depth-2 step
+ * (arguments as given to its gather): chunks set in d_prev_mask but not in
+ * d_sel_mask get g_t + 0; chunks set in d_prev2_mask and in neither later
+ * mask get g_t + (g_{t-1} + 0).  Afterwards d_residual holds the whole
+ * residual.  Harmless to later steps.  Errors as ga_residual_flush_layers.
+ */
+ga_status ga_residual_flush_layers2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                    const uint64_t* d_prev_layer_ptrs, float* d_residual,
+                                    const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
+                                    const uint32_t* d_prev2_mask, hipStream_t stream);
+
+/*
  * Momentum SGD on binary32 master weights, Caffe form (FireCaffe runs Caffe
  * models and reproduces Caffe's numbers [FC FAQ]), per element:
  *   v <- fl(fl(mu * v) + fl(lr * g));   w <- fl(w - v)

@@ -96,6 +96,9 @@ def test_calls_reject_null_plan_without_launching(ga):
     assert L.ga_sparse_gather_reduce_layers_pending(None, None, None, None, None, None, None, None, None,
                                                     None) == ga.GA_ERR_INVALID
     assert L.ga_residual_flush_layers(None, None, None, None, None, None) == ga.GA_ERR_INVALID
+    assert L.ga_chunk_norm_layers_pending2(*([None] * 10)) == ga.GA_ERR_INVALID
+    assert L.ga_sparse_gather_reduce_layers_pending2(*([None] * 12)) == ga.GA_ERR_INVALID
+    assert L.ga_residual_flush_layers2(*([None] * 8)) == ga.GA_ERR_INVALID
     assert L.ga_reduce_variant(None, None, 0, 0, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_tree_reduce_layers(None, None, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_chunk_norm_layers(None, None, None, None, None, None) == ga.GA_ERR_INVALID

@@ -46,25 +46,41 @@ def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False, mode="def
     wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
     rd, keys = plan.empty_residual(), plan.empty_keys()
     idx = torch.full((wl.W, max(k, 1)), -1, dtype=torch.int32, device="cuda")
-    masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(2)]
+    masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(3)]
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
     print("[%s] W=%d P=%d fp16=%s C=%d rho=%g %s" % (mode, wl.W, P, wl.fp16, C, wl.rho, mis), flush=True)
-    prev_layers = None      # the previous step's tensors, kept alive for the pending form
+    prev_layers = []        # the previous steps' tensors, kept alive for the pending forms
     for step in range(1, steps + 1):
         b = workloads.grad_bucket(wl, step, ld)
         if hook is not None:
             hook(b, step)
         res = oracle.sparse_step(b, P, wl.fp16, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
-        cur, prev = masks[step % 2], masks[(step + 1) % 2]
+        if mode.startswith("pending2"):
+            # three buffers in turn: cur holds the mask of three steps back
+            cur, prev, prev2 = masks[step % 3], masks[(step + 2) % 3], masks[(step + 1) % 3]
+        else:
+            cur, prev = masks[step % 2], masks[(step + 1) % 2]
         buf, ptrs = device_layers(b[:, :P], wl.numels, MIS[mis])
         r_view = rd
         if mode == "defer":
             plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
             plan.chunk_topk(keys, idx, cur)
             plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        elif mode.startswith("pending2"):
+            pptrs = prev_layers[-1][1] if prev_layers else ptrs
+            ppptrs = prev_layers[-2][1] if len(prev_layers) > 1 else ptrs
+            plan.chunk_norm_layers_pending2(ptrs, pptrs, ppptrs, rd, keys, prev, prev2, cur)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_pending2(ptrs, pptrs, rd, prev, cur, prev2, gd, wd, vd, wl.lr, wl.mu)
+            if mode == "pending2_flush":
+                plan.residual_flush_layers2(ptrs, pptrs, rd, prev, cur, prev2)
+            else:
+                r_view = rd.clone()
+                plan.residual_flush_layers2(ptrs, pptrs, r_view, prev, cur, prev2)
+            prev_layers = (prev_layers + [(buf, ptrs)])[-2:]
         else:
             # cur still holds the mask of two steps back (all zero at first)
-            pptrs = ptrs if prev_layers is None else prev_layers[1]
+            pptrs = prev_layers[-1][1] if prev_layers else ptrs
             plan.chunk_norm_layers_pending(ptrs, pptrs, rd, keys, prev, cur)
             plan.chunk_topk(keys, idx, cur)
             plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
@@ -73,7 +89,7 @@ def run_defer(ga, wl, mis="aligned", steps=4, hook=None, strict=False, mode="def
             else:
                 r_view = rd.clone()
                 plan.residual_flush_layers(ptrs, r_view, prev, cur)
-            prev_layers = (buf, ptrs)
+            prev_layers = [(buf, ptrs)]
         torch.cuda.synchronize()
         if wl.rho not in (0.0, 1.0):
             assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
@@ -117,6 +133,24 @@ def test_pending_matches_oracle(ga, fp16, W, numels, C, mis):
 
 
 @pytest.mark.parametrize("fp16", [False, True])
+@pytest.mark.parametrize("W,numels,C", [(1, [3000, 7, 2000], 256), (3, workloads.WORKLOADS["tiny"].numels, 512),
+                                        (16, [8, 1, 5000, 7, 4096, 333, 64], 256), (33, [20000, 37, 4003], 1024),
+                                        (128, [2048, 16, 4099, 520], 256), (300, [3000, 17, 1000], 512)])
+@pytest.mark.parametrize("mis", list(MIS))
+def test_pending2_matches_oracle(ga, fp16, W, numels, C, mis):
+    wl = workloads.custom(W, numels, fp16, sigma=1e-3, scale_mode="chunk", scale_log10=(-4.0, 0.0), chunk=C,
+                          rho=0.2)
+    run_defer(ga, wl, mis, steps=6, mode="pending2")
+
+
+@pytest.mark.parametrize("fp16", [False, True])
+def test_pending2_flushed_every_step(ga, fp16):
+    wl = workloads.custom(16, [8, 1, 5000, 7, 4096, 333, 64], fp16, sigma=1e-3, scale_mode="chunk",
+                          scale_log10=(-4.0, 0.0), chunk=256, rho=0.2)
+    run_defer(ga, wl, "mixed", steps=6, mode="pending2_flush")
+
+
+@pytest.mark.parametrize("fp16", [False, True])
 def test_pending_flushed_every_step(ga, fp16):
     """Flushing the live residual after every step changes nothing: the next
     norm pass computes the same pending values itself."""
@@ -125,7 +159,7 @@ def test_pending_flushed_every_step(ga, fp16):
     run_defer(ga, wl, "mixed", steps=5, mode="pending_flush")
 
 
-@pytest.mark.parametrize("mode", ["defer", "pending"])
+@pytest.mark.parametrize("mode", ["defer", "pending", "pending2"])
 @pytest.mark.parametrize("rho", [0.0, 1.0])
 def test_defer_keep_ratio_extremes(ga, rho, mode):
     wl = workloads.custom(6, [9000, 11, 300], True, sigma=1e-2, chunk=256, rho=rho)
@@ -138,11 +172,11 @@ def test_defer_negative_zero_leaves(ga):
     def hook(b, step):
         b[:, 100:300] = 0x8000          # binary16 -0 in every worker
         b[1:, 600:700] = 0x8000
-    for mode in ("defer", "pending"):
+    for mode in ("defer", "pending", "pending2"):
         wl = workloads.custom(4, [3000], True, sigma=1e-2, chunk=256, rho=1.0)
         run_defer(ga, wl, "aligned", steps=3, hook=hook, strict=True, mode=mode)
         wl = workloads.custom(4, [3000], True, sigma=1e-2, chunk=256, rho=0.5)
-        run_defer(ga, wl, "aligned", steps=4, hook=hook, strict=True, mode=mode)
+        run_defer(ga, wl, "aligned", steps=5, hook=hook, strict=True, mode=mode)
 
 
 def test_defer_errors(ga):
@@ -162,6 +196,13 @@ def test_defer_errors(ga):
     assert e.value.status == ga.GA_ERR_INVALID
     with pytest.raises(ga.GAError) as e:
         plan.sparse_gather_reduce_layers_pending(ptrs, rd, m0, m0, g)
+    assert e.value.status == ga.GA_ERR_INVALID
+    m2 = torch.zeros((4, plan.mask_words), dtype=torch.int32, device="cuda")
+    with pytest.raises(ga.GAError) as e:
+        plan.sparse_gather_reduce_layers_pending2(ptrs, ptrs, rd, m0, m1, m1, g)
+    assert e.value.status == ga.GA_ERR_INVALID
+    with pytest.raises(ga.GAError) as e:
+        plan.sparse_gather_reduce_layers_pending2(ptrs, ptrs, rd, m1, m1, m2, g)
     assert e.value.status == ga.GA_ERR_INVALID
     plan = ga.Plan(4, [1000], True, chunk=64, keep_ratio=0.5)
     rd = plan.empty_residual()

@@ -148,11 +148,11 @@ def test_buckets_alexnet16_full_size(ga, cap):
         log("alexnet16 buckets (cap %d) step %d ok in %.1fs" % (cap, step, time.time() - t0))
 
 
-@pytest.mark.parametrize("mode,steps", [("defer", 3), ("pending", 4)])
+@pytest.mark.parametrize("mode,steps", [("defer", 3), ("pending", 4), ("pending2", 5)])
 def test_sparse_alexnet128_full_size_deferred(ga, mode, steps):
     """The AlexNet-shaped W=128 sparse workload as benchmarked: 2048 per-layer
     tensors, consecutive steps in deferred lazy-zero mode (two mask buffers)
-    or its pending form (the previous step's tensors kept; the residual is
+    or its pending forms (the previous steps' tensors kept; the residual is
     compared through a flushed copy), every output compared with the oracle."""
     wl = workloads.WORKLOADS["alexnet128_sparse"]
     C = wl.chunk
@@ -166,10 +166,10 @@ def test_sparse_alexnet128_full_size_deferred(ga, mode, steps):
     rd = plan.empty_residual()
     keys = plan.empty_keys()
     idx = torch.empty((wl.W, k), dtype=torch.int32, device="cuda")
-    masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(2)]
+    masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(3)]
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
     sample = [0, 1, 63, 127]
-    prev_layers = None
+    prev_layers = []
     for step in range(1, steps + 1):
         t0 = time.time()
         b = workloads.grad_bucket(wl, step, ld, seg=seg)
@@ -177,19 +177,30 @@ def test_sparse_alexnet128_full_size_deferred(ga, mode, steps):
         res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         del b
         prev, cur = masks[(step + 1) % 2], masks[step % 2]
+        if mode == "pending2":
+            cur, prev, prev2 = masks[step % 3], masks[(step + 2) % 3], masks[(step + 1) % 3]
         r_view = rd
         if mode == "defer":
             plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
             plan.chunk_topk(keys, idx, cur)
             plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+        elif mode == "pending2":
+            pptrs = prev_layers[-1][1] if prev_layers else ptrs
+            ppptrs = prev_layers[-2][1] if len(prev_layers) > 1 else ptrs
+            plan.chunk_norm_layers_pending2(ptrs, pptrs, ppptrs, rd, keys, prev, prev2, cur)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_pending2(ptrs, pptrs, rd, prev, cur, prev2, gd, wd, vd, wl.lr, wl.mu)
+            r_view = rd.clone()
+            plan.residual_flush_layers2(ptrs, pptrs, r_view, prev, cur, prev2)
+            prev_layers = (prev_layers + [(buf, ptrs)])[-2:]
         else:
-            pptrs = ptrs if prev_layers is None else prev_layers[1]
+            pptrs = prev_layers[-1][1] if prev_layers else ptrs
             plan.chunk_norm_layers_pending(ptrs, pptrs, rd, keys, prev, cur)
             plan.chunk_topk(keys, idx, cur)
             plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
             r_view = rd.clone()
             plan.residual_flush_layers(ptrs, r_view, prev, cur)
-            prev_layers = (buf, ptrs)
+            prev_layers = [(buf, ptrs)]
         torch.cuda.synchronize()
         del buf
         assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
