@@ -305,35 +305,45 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
             }
             const int32_t gn = W - g0 < 64 ? W - g0 : 64;
             for (int32_t u0 = 0; u0 < gn; u0 += UNR) {
-                // y: the previous step's gradient of a pending leaf (binary16:
-                // 4 elements as raw bits in two words; binary32: 4 words)
+                // A pending leaf (P2) needs the previous step's gradient too:
+                // binary16 leaves hold both as raw bits, this step's in words
+                // 0-1 of x and the previous step's in words 2-3; binary32
+                // leaves keep the previous step's in y4.
                 v4u x[UNR];
-                v2u y2[P2 ? UNR : 1];
                 v4u y4[P2 && !FP16 ? UNR : 1];
 #pragma unroll
                 for (int u = 0; u < UNR; ++u) {
                     x[u] = v4u{0u, 0u, 0u, 0u};
-                    if (P2) {
-                        y2[u] = v2u{0u, 0u};
-                        if (!FP16) y4[u] = v4u{0u, 0u, 0u, 0u};
-                    }
+                    if (P2 && !FP16) y4[u] = v4u{0u, 0u, 0u, 0u};
                     const int32_t b = u0 + u;
                     if (b < gn && ((mc >> b) & 1ull) && valid) {
-                        if (((mp >> b) & 1ull) || (P2 && ((mq >> b) & 1ull)))
+                        const bool pend = P2 && ((mq >> b) & 1ull);
+                        if (pend && FP16) {
+                            v2u h0, h1;
+                            if (vec) {
+                                const v4u t = load_grad<FP16>(true, mine, b, byte_off, layer_ptrs, offsets, L, g0 + b,
+                                                              la, ea, i0, P);
+                                h0 = v2u{t.x, t.y};
+                            } else {
+                                h0 = grad4_slow_raw16(layer_ptrs, offsets, L, g0 + b, la, ea, i0, P);
+                            }
+                            if (vecq) {
+                                const v4u t = load_grad<FP16>(true, prv, b, byte_off, prev_layer_ptrs, offsets, L,
+                                                              g0 + b, la, ea, i0, P);
+                                h1 = v2u{t.x, t.y};
+                            } else {
+                                h1 = grad4_slow_raw16(prev_layer_ptrs, offsets, L, g0 + b, la, ea, i0, P);
+                            }
+                            x[u] = v4u{h0.x, h0.y, h1.x, h1.y};
+                        } else if (((mp >> b) & 1ull) || pend) {
                             x[u] = load_grad<FP16>(vec, mine, b, byte_off, layer_ptrs, offsets, L, g0 + b, la, ea,
                                                    i0, P);
-                        else
+                            if (pend)
+                                y4[FP16 ? 0 : u] = load_grad<FP16>(vecq, prv, b, byte_off, prev_layer_ptrs, offsets,
+                                                                   L, g0 + b, la, ea, i0, P);
+                        } else {
                             x[u] = __builtin_nontemporal_load(
                                 reinterpret_cast<const v4u*>(resid + (int64_t)(g0 + b) * ld + i0));
-                        if (P2 && ((mq >> b) & 1ull)) {
-                            if (FP16 && !vecq) {
-                                y2[u] = grad4_slow_raw16(prev_layer_ptrs, offsets, L, g0 + b, la, ea, i0, P);
-                            } else {
-                                const v4u t = load_grad<FP16>(vecq, prv, b, byte_off, prev_layer_ptrs, offsets, L,
-                                                              g0 + b, la, ea, i0, P);
-                                if (FP16) y2[u] = v2u{t.x, t.y};
-                                else y4[u] = t;
-                            }
                         }
                     }
                 }
@@ -342,17 +352,18 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
                     const int32_t b = u0 + u;
                     if (b < gn) {
                         const bool pend = P2 && ((mq >> b) & 1ull);
-                        const int kind =
-                            ((((mc & mp) >> b) & 1ull) || pend) ? (vec ? kGradVec : kReady) : kResid;
-                        float4 a = decode_leaf<FP16>(x[u], kind);
-                        if (P2 && pend) {
+                        float4 a;
+                        if (pend) {
                             // a = g0 + (g1 + 0): adding +0 to g0 as well changes
                             // nothing, since g1 + 0 is never -0
-                            // binary16: raw bits on both load paths
-                            const float4 r1 =
-                                FP16 ? decode_leaf<FP16>(v4u{y2[u].x, y2[u].y, 0u, 0u}, kGradVec)
-                                     : decode_leaf<FP16>(y4[FP16 ? 0 : u], vecq ? kGradVec : kReady);
+                            const float4 r1 = FP16 ? decode_leaf<FP16>(v4u{x[u].z, x[u].w, 0u, 0u}, kGradVec)
+                                                   : decode_leaf<FP16>(y4[FP16 ? 0 : u], vecq ? kGradVec : kReady);
+                            a = FP16 ? decode_leaf<FP16>(v4u{x[u].x, x[u].y, 0u, 0u}, kGradVec)
+                                     : decode_leaf<FP16>(x[u], vec ? kGradVec : kReady);
                             a.x += r1.x; a.y += r1.y; a.z += r1.z; a.w += r1.w;
+                        } else {
+                            const int kind = (((mc & mp) >> b) & 1ull) ? (vec ? kGradVec : kReady) : kResid;
+                            a = decode_leaf<FP16>(x[u], kind);
                         }
                         float f[E] = {a.x, a.y, a.z, a.w};
                         tree.push(f, cnt);
