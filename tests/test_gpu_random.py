@@ -3,7 +3,9 @@ path that applies to it and compared with the oracle element by element:
 random worker counts, layer lists (aligned and ragged sizes, small and large
 layers), binary16 or binary32 gradients, chunk sizes and keep ratios, both
 residual modes, zero-copy tensors at random misalignments, and multi-bucket
-schedules at random thresholds, the deferred residual form where it applies.
+schedules at random thresholds, the deferred residual form where it applies
+(plain, or pending at depth 1 or 2, its residual checked through a flushed
+copy).
 The case is printed before it runs."""
 import numpy as np
 import pytest
@@ -48,8 +50,9 @@ def draw(seed):
     deferred = bool(sparse and chunk % 256 == 0 and rng.random() < 0.7)
     mis = int(rng.integers(0, 4))
     thr = int(rng.choice([1, 64, 1024, 16384, 1 << 30]))
+    form = str(rng.choice(["defer", "pending", "pending2"])) if deferred else None
     return dict(W=W, numels=numels, fp16=fp16, sparse=sparse, chunk=chunk, rho=rho, lazy=lazy or deferred,
-                deferred=deferred, mis=mis, thr=thr)
+                deferred=deferred, mis=mis, thr=thr, form=form)
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
@@ -92,14 +95,33 @@ def test_random_case(ga, seed):
     wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
     rd, keys = plan.empty_residual(), plan.empty_keys()
     idx = torch.full((W, max(k, 1)), -1, dtype=torch.int32, device="cuda")
-    masks = [torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(2)]
+    masks = [torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(3)]
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
-    for step in (1, 2, 3):
+    kept = []               # the previous steps' tensors (pending forms)
+    form = c["form"]
+    for step in range(1, 5 if form in ("pending", "pending2") else 4):
         b = workloads.grad_bucket(wl, step, ld)
         res = oracle.sparse_step(b, P, fp16, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         cur, prev = masks[step % 2], masks[(step + 1) % 2]
+        if form == "pending2":
+            cur, prev, prev2 = masks[step % 3], masks[(step + 2) % 3], masks[(step + 1) % 3]
         buf, ptrs = device_layers(b[:, :P], numels, misalign)
-        if c["deferred"]:
+        r_view = rd
+        p1 = kept[-1][1] if kept else ptrs
+        p2 = kept[-2][1] if len(kept) > 1 else ptrs
+        if form == "pending":
+            plan.chunk_norm_layers_pending(ptrs, p1, rd, keys, prev, cur)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+            r_view = rd.clone()
+            plan.residual_flush_layers(ptrs, r_view, prev, cur)
+        elif form == "pending2":
+            plan.chunk_norm_layers_pending2(ptrs, p1, p2, rd, keys, prev, prev2, cur)
+            plan.chunk_topk(keys, idx, cur)
+            plan.sparse_gather_reduce_layers_pending2(ptrs, p1, rd, prev, cur, prev2, gd, wd, vd, wl.lr, wl.mu)
+            r_view = rd.clone()
+            plan.residual_flush_layers2(ptrs, p1, r_view, prev, cur, prev2)
+        elif form == "defer":
             plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
             plan.chunk_topk(keys, idx, cur)
             plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
@@ -107,6 +129,7 @@ def test_random_case(ga, seed):
             plan.chunk_norm_layers(ptrs, rd, keys, prev if (c["lazy"] and step > 1) else None)
             plan.chunk_topk(keys, idx, cur)
             plan.sparse_gather_reduce(rd, cur, not c["lazy"], gd, wd, vd, wl.lr, wl.mu)
+        kept = (kept + [(buf, ptrs)])[-2:]
         torch.cuda.synchronize()
         if not np.all(res.margin > 1e-12):
             pytest.skip("selection boundary too close to certify at seed %d" % seed)
@@ -114,7 +137,7 @@ def test_random_case(ga, seed):
         if k > 0:
             assert np.array_equal(host(idx)[:, :k], res.sel_idx), "selected chunk indices differ"
         assert np.array_equal(host(cur).view(np.uint32), res.sel_mask)
-        r_got = host(rd)
+        r_got = host(r_view)
         if c["lazy"]:
             m = host(cur).view(np.uint32).astype(np.int64)
             ch = np.arange(n_c)
