@@ -719,6 +719,7 @@ def deferred_bytes(plan, prev, cur, P, b_in):
                                                                  ("materialized", bp & ~bc))}
     return {"chunks_resent": counts["resent"], "chunks_new": counts["new"],
             "chunks_materialized": counts["materialized"],
+            "chunks_sent_by_any_worker": int(bc.any(dim=0).sum()), "n_chunks": int(n_c),
             "gather_bytes": int(elems["resent"] * b_in + elems["new"] * 4 + 16 * P),
             "materialize_bytes": int(elems["materialized"] * (b_in + 4))}
 
