@@ -110,8 +110,9 @@ __device__ __forceinline__ void epilogue(const float (&s)[E], int64_t i0, int64_
                 sgd_update(g[4 * q + 1], lr, mu, wv.y, vv.y);
                 sgd_update(g[4 * q + 2], lr, mu, wv.z, vv.z);
                 sgd_update(g[4 * q + 3], lr, mu, wv.w, vv.w);
-                *reinterpret_cast<float4*>(w + i0 + 4 * q) = wv;
-                *reinterpret_cast<float4*>(v + i0 + 4 * q) = vv;
+                // streaming stores: w and v are not read again within the step
+                __builtin_nontemporal_store(f32x4{wv.x, wv.y, wv.z, wv.w}, reinterpret_cast<f32x4*>(w + i0 + 4 * q));
+                __builtin_nontemporal_store(f32x4{vv.x, vv.y, vv.z, vv.w}, reinterpret_cast<f32x4*>(v + i0 + 4 * q));
             }
         }
     } else {
