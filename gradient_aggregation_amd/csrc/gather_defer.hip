@@ -185,13 +185,12 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
     uint64_t mq0 = 0ull, mq1 = 0ull, mq2 = 0ull, mq3 = 0ull;
     bool any_sent = false, any_resent = false, any_pend = false;
     if (kCached) {
-        uint32_t sw[4], pw[4], qw[4];
+        uint32_t sw[4], pw[4];
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const int32_t wk = gi * 64 + lane;
             sw[gi] = wk < W ? sel_mask[(int64_t)wk * mw + cw] : 0u;
             pw[gi] = wk < W ? prev_mask[(int64_t)wk * mw + cw] : 0u;
-            qw[gi] = P2 && wk < W ? prev2_mask[(int64_t)wk * mw + cw] : 0u;
         }
         mc0 = __ballot((sw[0] & cb) != 0u);
         mc1 = __ballot((sw[1] & cb) != 0u);
@@ -205,8 +204,15 @@ __global__ __launch_bounds__(kThreads) void k_gather_defer(
         // some worker sent the chunk now and in the previous step: its leaf is
         // read from the gradient tensor
         any_resent = ((mc0 & mp0) | (mc1 & mp1) | (mc2 & mp2) | (mc3 & mp3)) != 0ull;
-        if (P2) {
-            // pending (sent two steps back, not in the previous step) and sent now
+        if (P2 && any_sent) {
+            // pending (sent two steps back, not in the previous step) and sent
+            // now; the words of two steps back only where a leaf is sent
+            uint32_t qw[4];
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int32_t wk = gi * 64 + lane;
+                qw[gi] = wk < W ? prev2_mask[(int64_t)wk * mw + cw] : 0u;
+            }
             mq0 = __ballot((qw[0] & cb) != 0u) & mc0 & ~mp0;
             mq1 = __ballot((qw[1] & cb) != 0u) & mc1 & ~mp1;
             mq2 = __ballot((qw[2] & cb) != 0u) & mc2 & ~mp2;
