@@ -17,7 +17,12 @@
 //     exactly what the non-deferred lazy mode leaves (k_materialize).
 // In the pending form the last part is left out: that residual stays held as
 // the step's gradient, which the next step's norm pass reads in its place;
-// launch_residual_flush writes it when the buffer itself is wanted.
+// launch_residual_flush writes it when the buffer itself is wanted.  In the
+// depth-2 pending form (P2) the norm pass also left unstored the a of a chunk
+// sent two steps back and not in the previous step; if that chunk is sent now,
+// its leaf is recomputed here as g + (g' + 0) from this and the previous
+// step's tensors (k_gather_pending2), and if not, the next norm pass or the
+// flush (k_materialize<FP16, true>) forms it.
 #include "device.h"
 #include "plan.h"
 #include "tree.h"
