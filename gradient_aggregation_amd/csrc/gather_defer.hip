@@ -21,7 +21,7 @@
 // depth-2 pending form (P2) the norm pass also left unstored the a of a chunk
 // sent two steps back and not in the previous step; if that chunk is sent now,
 // its leaf is recomputed here as g + (g' + 0) from this and the previous
-// step's tensors (k_gather_pending2), and if not, the next norm pass or the
+// step's tensors (k_gather_defer<LEV, FP16, true>), and if not, the next norm pass or the
 // flush (k_materialize<FP16, true>) forms it.
 #include "device.h"
 #include "plan.h"
