@@ -331,6 +331,13 @@ def main():
     if pending2:
         tl = n_steps - 1
         deferred_last = deferred_bytes(plan, masks[(tl + 2) % 3], masks[tl % 3], P, b_in)
+        # chunks whose residual is still held as the last two steps' gradients
+        sh = torch.arange(32, device="cuda", dtype=torch.int32)
+
+        def bits(m):
+            return (((m.unsqueeze(-1) >> sh) & 1) != 0).reshape(m.shape[0], -1)[:, :plan.n_chunks]
+        held2 = bits(masks[(tl + 1) % 3]) & ~bits(masks[(tl + 2) % 3]) & ~bits(masks[tl % 3])
+        deferred_last["chunks_pending_two_steps"] = int(held2.sum())
     else:
         deferred_last = deferred_bytes(plan, masks[(n_steps - 1) % 2], masks[n_steps % 2], P, b_in) if defer else None
     if pending:
