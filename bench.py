@@ -4,19 +4,16 @@
 Default workload: AlexNet-shaped, W=128 workers x P=60,965,224 parameters,
 binary16 gradients, coarse-grained sparse communication with 32768-element
 chunks keeping 10% of them per worker (k=187 of 1861), the residual carried in
-lazy-zero mode (by default in its deferred, depth-2 pending form: a chunk
-sent in the previous step stores no a and the gather reads its gradient; if it
-is not sent again, its residual stays held as that gradient, and one step
-later as the sum of the two gradients, which the next passes recompute; so the
-gradient tensors of the previous two steps are kept), and momentum SGD on
-binary32 master weights.
+deferred form (written every depth+1 steps and re-formed in between from the
+previous `depth` gradient batches and selection masks, which are kept), and
+momentum SGD on binary32 master weights.
 
 One step = lazy-allreduce fusion of the W*16 per-layer gradient tensors read
 with zero copy through the layer table, together with the chunk norms and the
-residual (k_chunk_norm), top-k chunk selection (k_topk), and the gather-reduce
-of the selected chunks fused with the mean and the SGD update (k_gather_defer,
+residual (k_norm_hist), top-k chunk selection (k_topk), and the gather-reduce
+of the selected chunks fused with the mean and the SGD update (k_gather_hist,
 or k_gather_wave with --residual lazy), over one batch of gradients already
-resident in HBM (three gradient batches are cycled so that consecutive steps
+resident in HBM (six gradient batches are cycled so that consecutive steps
 see fresh inputs).
 
 Prints one JSON line:
@@ -54,18 +51,19 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20 for the sparse workload, 200 for a dense one)")
-    ap.add_argument("--warmup", type=int, default=5)
+                    help="timed steps (default 24 for the sparse workload, a whole number of store periods "
+                         "at depth 0-3; 200 for a dense one)")
+    ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--workload", default="alexnet128_sparse")
-    ap.add_argument("--batches", type=int, default=3, help="distinct gradient batches cycled over steps")
+    ap.add_argument("--batches", type=int, default=6, help="distinct gradient batches cycled over steps")
     ap.add_argument("--source", choices=["layers", "bucket"], default="layers",
                     help="gradients as per-layer tensors fused with zero copy (default) or a packed bucket")
-    ap.add_argument("--residual", choices=["pending2", "pending", "deferred", "lazy"], default="pending2",
-                    help="sparse workload: lazy-zero residual with one mask buffer, or its deferred form (chunks "
-                         "sent in the previous step store no a; the gather reads their gradient), or the pending "
-                         "form of that (the residual of a chunk sent in the previous step but not now stays held "
-                         "as the step's gradient, which the next step's norm pass reads), or its depth-2 form (a chunk pending one "
-                         "step stores no a either; the previous two gradient batches are kept)")
+    ap.add_argument("--residual", choices=["deferred", "lazy"], default="deferred",
+                    help="sparse workload: the deferred residual (written every depth+1 steps, re-formed from the "
+                         "held gradients in between) or the lazy-zero sequence of the boundary's calls")
+    ap.add_argument("--depth", type=int, default=1,
+                    help="deferred residual: earlier gradient batches held (the residual is stored every depth+1 "
+                         "steps)")
     ap.add_argument("--order", choices=["tree", "server", "ring"], default="tree",
                     help="dense workloads: summation order (parameter server, ring) for comparison")
     ap.add_argument("--wire", choices=["f32", "f16"], default="f32",
@@ -153,7 +151,7 @@ def main():
     wl = workloads.WORKLOADS[args.workload]
     sparse = wl.mode == "sparse"
     if args.steps is None:
-        args.steps = 20 if sparse else 200
+        args.steps = 24 if sparse else 200
     variant = args.order != "tree" or args.wire != "f32"
     if variant:
         if sparse:
@@ -218,78 +216,50 @@ def main():
     gen_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
-    defer = pending = pending2 = False
+    deferred = False
     if sparse:
-        rd = plan.empty_residual()
-        keys = plan.empty_keys()
-        idx = torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda")
-        mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
-        # deferred mode: two mask buffers swap roles (previous / current step)
-        masks = [mask, torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")]
-        defer = args.residual in ("deferred", "pending", "pending2") and layers_src and plan.chunk % 256 == 0
-        pending = defer and args.residual in ("pending", "pending2")
-        pending2 = defer and args.residual == "pending2"
-        if pending2:
-            masks.append(torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda"))
+        deferred = args.residual == "deferred" and layers_src and plan.chunk % 256 == 0
+        if args.residual == "deferred" and not deferred:
+            log("the deferred form needs per-layer tensors and a chunk size that is a multiple of 256; "
+                "timing the lazy-zero sequence")
+        if deferred and nb < args.depth + 1:
+            print("--depth %d needs at least %d gradient batches" % (args.depth, args.depth + 1), file=sys.stderr)
+            sys.exit(2)
         names = ["chunk_norm", "topk", "gather_sgd"]
     else:
         names = ["tree_sgd"]
     n_steps = args.warmup + args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_steps)]
+    stored = [False] * n_steps
 
-    def step(t: int, rec: bool):
+    if sparse and deferred:
+        dr = ga.DeferredResidual(plan, args.depth)
+    elif sparse:
+        rd = plan.empty_residual()
+        keys = plan.empty_keys()
+        idx = torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda")
+        mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
+
+    def step(t: int):
         b = sources[t % nb]
         wd, vd = states[t % n_state]
         e = ev[t]
-        if rec:
-            e[0].record(stream)
-        if sparse and pending2:
-            # three mask buffers in turn (cur holds the mask of three steps
-            # back); the gradient tensors of the previous two batches
-            cur, prev, prev2 = masks[t % 3], masks[(t + 2) % 3], masks[(t + 1) % 3]
-            g1 = sources[(t - 1) % nb] if t > 0 else b
-            g2 = sources[(t - 2) % nb] if t > 1 else b
-            plan.chunk_norm_layers_pending2(b, g1, g2, rd, keys, prev, prev2, cur)
-            if rec:
-                e[1].record(stream)
-            plan.chunk_topk(keys, idx, cur)
-            if rec:
-                e[2].record(stream)
-            plan.sparse_gather_reduce_layers_pending2(b, g1, rd, prev, cur, prev2, None, wd, vd, wl.lr, wl.mu)
-            if rec:
-                e[3].record(stream)
-        elif sparse and defer:
-            prev, cur = masks[t % 2], masks[(t + 1) % 2]
-            if pending:
-                # cur still holds the mask of two steps back; the previous
-                # step's gradient tensors are those of the previous batch
-                plan.chunk_norm_layers_pending(b, sources[(t - 1) % nb] if t > 0 else b, rd, keys, prev, cur)
-            else:
-                plan.chunk_norm_layers_defer(b, rd, keys, prev)
-            if rec:
-                e[1].record(stream)
-            plan.chunk_topk(keys, idx, cur)
-            if rec:
-                e[2].record(stream)
-            if pending:
-                plan.sparse_gather_reduce_layers_pending(b, rd, prev, cur, None, wd, vd, wl.lr, wl.mu)
-            else:
-                plan.sparse_gather_reduce_layers_defer(b, rd, prev, cur, None, wd, vd, wl.lr, wl.mu)
-            if rec:
-                e[3].record(stream)
+        e[0].record(stream)
+        if sparse and deferred:
+            stored[t] = dr.step(b, None, wd, vd, wl.lr, wl.mu, events=e[1:])
         elif sparse:
+            # the lazy-zero sequence of the boundary's calls: norms (zero-copy or
+            # from a bucket), top-k, gather-reduce without zeroing
             if layers_src:
                 plan.chunk_norm_layers(b, rd, keys, mask if t > 0 else None)
             else:
                 plan.chunk_norm(b, rd, keys, mask if t > 0 else None)
-            if rec:
-                e[1].record(stream)
+            e[1].record(stream)
             plan.chunk_topk(keys, idx, mask)
-            if rec:
-                e[2].record(stream)
+            e[2].record(stream)
             plan.sparse_gather_reduce(rd, mask, False, None, wd, vd, wl.lr, wl.mu)
-            if rec:
-                e[3].record(stream)
+            e[3].record(stream)
+            stored[t] = True
         else:
             if variant:
                 plan.reduce_variant(b, args.order, args.wire == "f16", None, wd, vd, wl.lr, wl.mu)
@@ -297,11 +267,10 @@ def main():
                 plan.tree_reduce_layers(b, None, wd, vd, wl.lr, wl.mu)
             else:
                 plan.tree_reduce(b, None, wd, vd, wl.lr, wl.mu)
-            if rec:
-                e[1].record(stream)
+            e[1].record(stream)
 
     for t in range(args.warmup):
-        step(t, True)
+        step(t)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -309,7 +278,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for t in range(args.warmup, n_steps):
-        step(t, True)
+        step(t)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -317,34 +286,28 @@ def main():
     # overheads included); gpu_ms_per_step is the HIP-event span on the stream
     gpu_ms_step = t_start.elapsed_time(t_end) / args.steps
     ms_step = wall * 1e3 / args.steps
-    # the first step (no previous selection mask: the whole residual is read)
     first_step = {nm: round(ev[0][j].elapsed_time(ev[0][j + 1]), 4) for j, nm in enumerate(names)}
     per_kernel = {}
+    timed = range(args.warmup, n_steps)
     for j, nm in enumerate(names):
-        d = [ev[t][j].elapsed_time(ev[t][j + 1]) for t in range(args.warmup, n_steps)]
+        d = [ev[t][j].elapsed_time(ev[t][j + 1]) for t in timed]
         per_kernel[nm] = {"mean_ms": float(np.mean(d)), "min_ms": float(np.min(d)), "max_ms": float(np.max(d))}
+        if sparse and deferred and args.depth > 0:
+            for kind, want in (("storing", True), ("other", False)):
+                dk = [ev[t][j].elapsed_time(ev[t][j + 1]) for t in timed if stored[t] == want]
+                if dk:
+                    per_kernel[nm]["mean_ms_%s_steps" % kind] = round(float(np.mean(dk)), 4)
     log("timed %d steps: %.3f ms/step (GPU events %.3f ms/step); %s" % (
         args.steps, ms_step, gpu_ms_step,
         ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
 
     b_in = 2 if wl.fp16 else 4
-    if pending2:
-        tl = n_steps - 1
-        deferred_last = deferred_bytes(plan, masks[(tl + 2) % 3], masks[tl % 3], P, b_in)
-        # chunks whose residual is still held as the last two steps' gradients
-        sh = torch.arange(32, device="cuda", dtype=torch.int32)
-
-        def bits(m):
-            return (((m.unsqueeze(-1) >> sh) & 1) != 0).reshape(m.shape[0], -1)[:, :plan.n_chunks]
-        held2 = bits(masks[(tl + 1) % 3]) & ~bits(masks[(tl + 2) % 3]) & ~bits(masks[tl % 3])
-        deferred_last["chunks_pending_two_steps"] = int(held2.sum())
-    else:
-        deferred_last = deferred_bytes(plan, masks[(n_steps - 1) % 2], masks[n_steps % 2], P, b_in) if defer else None
-    if pending:
-        # nothing is materialized: those chunks' residuals stay pending and
-        # the next norm pass reads them as gradient (b_in per element)
-        deferred_last["chunks_pending"] = deferred_last.pop("chunks_materialized")
-        deferred_last["pending_read_bytes_next_step"] = deferred_last.pop("materialize_bytes") // (b_in + 4) * b_in
+    sel_stats = None
+    if sparse and deferred:
+        sel_stats = selection_stats(plan, dr.masks[(dr.next - 2) % len(dr.masks)],
+                                    dr.masks[(dr.next - 1) % len(dr.masks)], P)
+    elif sparse:
+        sel_stats = selection_stats(plan, None, mask, P)
 
     pack = time_pack(plan, wl, sources[-1], keep[-1] if layers_src else None, stream)
 
@@ -368,11 +331,15 @@ def main():
         per_kernel[nm]["frac_hbm_peak"] = round(per_kernel[nm]["GBps_alg"] / HBM_PEAK_GBPS, 4)
     dom_ms = per_kernel[dom]["mean_ms"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    dom_kernel = ("k_chunk_norm" if sparse else "k_tree_layers" if layers_src else "k_tree") if not variant \
-        else "k_variant_" + ("tree" if args.order == "tree" else "seq")
+    if sparse:
+        dom_kernel = "k_norm_hist" if (deferred or layers_src) else "k_chunk_norm"
+    elif variant:
+        dom_kernel = "k_variant_" + ("tree" if args.order == "tree" else "seq")
+    else:
+        dom_kernel = "k_tree_layers" if layers_src else "k_tree"
     traffic_key = dom_kernel if not variant else "%s_order_%s_wire_%s" % (dom_kernel, args.order, args.wire)
-    if defer:
-        traffic_key = dom_kernel + ("_pending2" if pending2 else "_pending" if pending else "_deferred")
+    if sparse and deferred:
+        traffic_key = "%s_depth%d" % (dom_kernel, args.depth)
     traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
                                traffic_key)
 
@@ -395,9 +362,8 @@ def main():
             "accumulate": "f32 fixed binary tree", "keys": "f64" if sparse else None,
             "chunk": plan.chunk or None, "keep_ratio": wl.rho if sparse else None,
             "k": plan.k if sparse else None, "n_chunks": plan.n_chunks if sparse else None,
-            "residual_mode": (("depth-2 pending deferred lazy-zero" if pending2 else
-                               "pending deferred lazy-zero" if pending else "deferred lazy-zero") if defer
-                              else "lazy-zero") if sparse else None,
+            "residual_mode": (("deferred, depth %d (stored every %d steps)" % (args.depth, args.depth + 1))
+                              if deferred else "lazy-zero") if sparse else None,
             "gradient_batches": nb,
             "fusion": "zero-copy read of %d per-layer tensors" % (W * len(wl.numels)) if layers_src
                       else "pre-packed bucket",
@@ -411,7 +377,7 @@ def main():
         "grad_input_GBps": round(W * P * b_in / (ms_step * 1e-3) / 1e9, 2),
         "kernels": per_kernel,
         "first_step_ms": first_step if sparse else None,
-        "deferred_last_step": deferred_last,
+        "selection_last_step": sel_stats,
         "roofline": {
             "kernel": dom_kernel,
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -420,6 +386,8 @@ def main():
             # the bytes the kernel moves (counters) over its time, beside the
             # algorithmic figure above
             "moved_GBps": None if traffic is None else round(traffic["bytes_per_launch"] / (dom_ms * 1e-3) / 1e9, 1),
+            "moved_frac": None if traffic is None else round(
+                traffic["bytes_per_launch"] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic_source": None if traffic is None else traffic["summary"],
             "bytes_per_launch": dom_bytes, "mean_launch_ms": round(dom_ms, 4),
             # the same chip's plain-copy rate in this run (the fusion copy of the
@@ -705,30 +673,22 @@ def time_pack(plan, wl, src, layer_tensors, stream):
             "bytes": moved, "matches_source": ok}
 
 
-def deferred_bytes(plan, prev, cur, P, b_in):
-    """Chunk counts of one deferred step from its two selection masks, and the
-    bytes its gather and materialization move: a chunk sent again is read from
-    the gradient (b_in per element), a newly sent one from the residual (4),
-    and a chunk sent before but not now is copied into the residual (b_in + 4);
-    the gather also reads and writes w and v (16 per element)."""
+def selection_stats(plan, prev, cur, P):
+    """Chunk counts of one step's selection (cur) against the previous step's
+    (prev, or None): (worker, chunk) pairs sent, sent again, newly sent, and
+    the chunks some worker sent."""
     import torch
-    n_c, C = plan.n_chunks, plan.chunk
-    sh = torch.arange(32, device=prev.device, dtype=torch.int32)
+    n_c = plan.n_chunks
+    sh = torch.arange(32, device=cur.device, dtype=torch.int32)
 
     def bits(m):
         return (((m.unsqueeze(-1) >> sh) & 1) != 0).reshape(m.shape[0], -1)[:, :n_c]
 
-    bp, bc = bits(prev), bits(cur)
-    lens = torch.full((n_c,), C, dtype=torch.float64, device=prev.device)
-    lens[-1] = P - (n_c - 1) * C
-    counts = {nm: int(m.sum()) for nm, m in (("resent", bp & bc), ("new", bc & ~bp), ("materialized", bp & ~bc))}
-    elems = {nm: float((m.double() * lens).sum()) for nm, m in (("resent", bp & bc), ("new", bc & ~bp),
-                                                                 ("materialized", bp & ~bc))}
-    return {"chunks_resent": counts["resent"], "chunks_new": counts["new"],
-            "chunks_materialized": counts["materialized"],
-            "chunks_sent_by_any_worker": int(bc.any(dim=0).sum()), "n_chunks": int(n_c),
-            "gather_bytes": int(elems["resent"] * b_in + elems["new"] * 4 + 16 * P),
-            "materialize_bytes": int(elems["materialized"] * (b_in + 4))}
+    bc = bits(cur)
+    bp = bits(prev) if prev is not None else torch.zeros_like(bc)
+    return {"pairs_sent": int(bc.sum()), "pairs_sent_again": int((bp & bc).sum()),
+            "pairs_newly_sent": int((bc & ~bp).sum()), "chunks_sent_by_any_worker": int(bc.any(dim=0).sum()),
+            "n_chunks": int(n_c)}
 
 
 def measured_traffic(path, kernel):

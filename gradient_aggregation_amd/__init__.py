@@ -43,6 +43,15 @@ class SGD(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("mu", ctypes.c_float)]
 
 
+MAX_AGE = 2
+
+
+class History(ctypes.Structure):
+    """ga_history: what a deferred step holds of its residual (see gradagg.h)."""
+    _fields_ = [("age", ctypes.c_int32), ("d_masks", ctypes.c_void_p * (MAX_AGE + 1)),
+                ("d_layer_ptrs", ctypes.c_void_p * MAX_AGE)]
+
+
 _VP = ctypes.c_void_p
 _lib = None
 
@@ -95,25 +104,13 @@ def lib() -> ctypes.CDLL:
         L.ga_tree_combine.argtypes = [_VP, _VP, ctypes.c_int32, _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
         L.ga_sgd_momentum_apply.restype = st
         L.ga_sgd_momentum_apply.argtypes = [ctypes.c_int64, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP]
-        L.ga_chunk_norm_layers_defer.restype = st
-        L.ga_chunk_norm_layers_defer.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
-        L.ga_sparse_gather_reduce_layers_defer.restype = st
-        L.ga_sparse_gather_reduce_layers_defer.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(SGD), _VP,
-                                                           _VP, _VP]
-        L.ga_chunk_norm_layers_pending.restype = st
-        L.ga_chunk_norm_layers_pending.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
-        L.ga_sparse_gather_reduce_layers_pending.restype = st
-        L.ga_sparse_gather_reduce_layers_pending.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(SGD),
-                                                             _VP, _VP, _VP]
-        L.ga_residual_flush_layers.restype = st
-        L.ga_residual_flush_layers.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP]
-        L.ga_chunk_norm_layers_pending2.restype = st
-        L.ga_chunk_norm_layers_pending2.argtypes = [_VP] * 10
-        L.ga_sparse_gather_reduce_layers_pending2.restype = st
-        L.ga_sparse_gather_reduce_layers_pending2.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                                              ctypes.POINTER(SGD), _VP, _VP, _VP]
-        L.ga_residual_flush_layers2.restype = st
-        L.ga_residual_flush_layers2.argtypes = [_VP] * 8
+        L.ga_chunk_norm_deferred.restype = st
+        L.ga_chunk_norm_deferred.argtypes = [_VP, _VP, ctypes.POINTER(History), ctypes.c_int32, _VP, _VP, _VP]
+        L.ga_sparse_gather_reduce_deferred.restype = st
+        L.ga_sparse_gather_reduce_deferred.argtypes = [_VP, _VP, ctypes.POINTER(History), ctypes.c_int32, _VP, _VP,
+                                                       _VP, ctypes.POINTER(SGD), _VP, _VP, _VP]
+        L.ga_residual_flush.restype = st
+        L.ga_residual_flush.argtypes = [_VP, _VP, ctypes.POINTER(History), ctypes.c_int32, _VP, _VP, _VP]
         L.ga_bucket_boundaries.restype = st
         L.ga_bucket_boundaries.argtypes = [ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int64, _VP, _VP]
         L.ga_buckets_create.restype = st
@@ -318,115 +315,57 @@ class Plan:
                                           _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
                                           _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
 
-    def chunk_norm_layers_defer(self, layer_ptrs, resid, keys, prev_mask) -> None:
-        """Deferred-residual chunk norms: chunks set in prev_mask do not store a."""
+    def history(self, masks, layer_tables=()):
+        """A ga_history: masks[j] = selection of step t-1-j (int32 [W][mw]
+        tensor or None), j = 0..age; layer_tables[j] = layer table of step
+        t-1-j, j = 0..age-1.  age = len(masks) - 1."""
         torch = _torch()
-        L = len(self.layer_numels)
-        _check(lib().ga_chunk_norm_layers_defer(
-            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
-            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
+        age = len(masks) - 1
+        if age < 0 or age > MAX_AGE:
+            raise ValueError("history needs 1..%d masks" % (MAX_AGE + 1))
+        if len(layer_tables) != age:
+            raise ValueError("age %d needs %d earlier layer tables, got %d" % (age, age, len(layer_tables)))
+        h = History()
+        h.age = age
+        n = self.W * len(self.layer_numels)
+        for j, m in enumerate(masks):
+            h.d_masks[j] = _dev(m, torch.int32, self.W * self.mask_words, "mask %d" % j)
+        for j, t in enumerate(layer_tables):
+            h.d_layer_ptrs[j] = _dev(t, torch.int64, n, "layer table %d" % j)
+        return h
 
-    def sparse_gather_reduce_layers_defer(self, layer_ptrs, resid, prev_mask, sel_mask, grad=None, w=None, v=None,
-                                          lr: Optional[float] = None, mu: Optional[float] = None) -> None:
-        """Deferred-residual gather-reduce (reads the gradient tensors for
-        chunks sent now and in the previous step)."""
+    def chunk_norm_deferred(self, layer_ptrs, hist, store: bool, resid, keys) -> None:
+        """Deferred-residual norm pass of one step (hist from history())."""
         torch = _torch()
-        L = len(self.layer_numels)
+        n = self.W * len(self.layer_numels)
+        _check(lib().ga_chunk_norm_deferred(self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
+                                            ctypes.byref(hist), int(bool(store)),
+                                            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+                                            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"),
+                                            _stream_ptr()))
+
+    def sparse_gather_reduce_deferred(self, layer_ptrs, hist, stored: bool, resid, sel_mask, grad=None, w=None,
+                                      v=None, lr: Optional[float] = None, mu: Optional[float] = None) -> None:
+        """Deferred-residual gather-reduce of one step (hist and stored as given
+        to its norm pass)."""
+        torch = _torch()
+        n = self.W * len(self.layer_numels)
         sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
-        _check(lib().ga_sparse_gather_reduce_layers_defer(
-            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
+        _check(lib().ga_sparse_gather_reduce_deferred(
+            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"), ctypes.byref(hist), int(bool(stored)),
             _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
             _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
             _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
 
-    def chunk_norm_layers_pending(self, layer_ptrs, prev_layer_ptrs, resid, keys, prev_mask, prev2_mask) -> None:
-        """Pending-residual chunk norms: as chunk_norm_layers_defer, and chunks
-        set in prev2_mask but not in prev_mask take the previous step's
-        gradient (prev_layer_ptrs) + 0 as their residual."""
-        torch = _torch()
-        L = len(self.layer_numels)
-        _check(lib().ga_chunk_norm_layers_pending(
-            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
-            _dev(prev_layer_ptrs, torch.int64, self.W * L, "prev_layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
-            _dev(prev2_mask, torch.int32, self.W * self.mask_words, "prev2_mask"),
-            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
-
-    def sparse_gather_reduce_layers_pending(self, layer_ptrs, resid, prev_mask, sel_mask, grad=None, w=None,
-                                            v=None, lr: Optional[float] = None, mu: Optional[float] = None) -> None:
-        """The deferred gather-reduce without writing the residual of chunks
-        sent in the previous step but not now (it stays pending)."""
-        torch = _torch()
-        L = len(self.layer_numels)
-        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
-        _check(lib().ga_sparse_gather_reduce_layers_pending(
-            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
-            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
-            _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
-            _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
-
-    def residual_flush_layers(self, layer_ptrs, resid, prev_mask, sel_mask) -> None:
-        """Write the pending residuals of a step (chunks set in prev_mask but
-        not in sel_mask get the widened gradient + 0)."""
-        torch = _torch()
-        L = len(self.layer_numels)
-        _check(lib().ga_residual_flush_layers(
-            self._h, _dev(layer_ptrs, torch.int64, self.W * L, "layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
-            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
-
-    def chunk_norm_layers_pending2(self, layer_ptrs, prev_layer_ptrs, prev2_layer_ptrs, resid, keys, prev_mask,
-                                   prev2_mask, prev3_mask) -> None:
-        """Depth-2 pending chunk norms (masks of the previous three steps,
-        gradient tensors of the previous two)."""
+    def residual_flush(self, layer_ptrs, hist, stored: bool, resid, sel_mask) -> None:
+        """Write the residual after a deferred step (zero on the sent chunks)."""
         torch = _torch()
         n = self.W * len(self.layer_numels)
-        mwn = self.W * self.mask_words
-        _check(lib().ga_chunk_norm_layers_pending2(
-            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
-            _dev(prev_layer_ptrs, torch.int64, n, "prev_layer_ptrs"),
-            _dev(prev2_layer_ptrs, torch.int64, n, "prev2_layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, mwn, "prev_mask"), _dev(prev2_mask, torch.int32, mwn, "prev2_mask"),
-            _dev(prev3_mask, torch.int32, mwn, "prev3_mask"),
-            _dev(keys, torch.float64, self.W * self.n_chunks, "keys"), _stream_ptr()))
-
-    def sparse_gather_reduce_layers_pending2(self, layer_ptrs, prev_layer_ptrs, resid, prev_mask, sel_mask,
-                                             prev2_mask, grad=None, w=None, v=None, lr: Optional[float] = None,
-                                             mu: Optional[float] = None) -> None:
-        """Depth-2 pending gather-reduce."""
-        torch = _torch()
-        n = self.W * len(self.layer_numels)
-        mwn = self.W * self.mask_words
-        sgd = None if lr is None else ctypes.byref(SGD(lr, mu))
-        _check(lib().ga_sparse_gather_reduce_layers_pending2(
-            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
-            _dev(prev_layer_ptrs, torch.int64, n, "prev_layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, mwn, "prev_mask"), _dev(sel_mask, torch.int32, mwn, "sel_mask"),
-            _dev(prev2_mask, torch.int32, mwn, "prev2_mask"),
-            _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
-            _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
-
-    def residual_flush_layers2(self, layer_ptrs, prev_layer_ptrs, resid, prev_mask, sel_mask, prev2_mask) -> None:
-        """Write the pending residuals of a depth-2 step."""
-        torch = _torch()
-        n = self.W * len(self.layer_numels)
-        mwn = self.W * self.mask_words
-        _check(lib().ga_residual_flush_layers2(
-            self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"),
-            _dev(prev_layer_ptrs, torch.int64, n, "prev_layer_ptrs"),
-            _dev(resid, torch.float32, self.W * self.ld, "resid"),
-            _dev(prev_mask, torch.int32, mwn, "prev_mask"), _dev(sel_mask, torch.int32, mwn, "sel_mask"),
-            _dev(prev2_mask, torch.int32, mwn, "prev2_mask"), _stream_ptr()))
+        _check(lib().ga_residual_flush(self._h, _dev(layer_ptrs, torch.int64, n, "layer_ptrs"), ctypes.byref(hist),
+                                       int(bool(stored)), _dev(resid, torch.float32, self.W * self.ld, "resid"),
+                                       _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"),
+                                       _stream_ptr()))
 
     def chunk_norm(self, bucket, resid, keys, prev_mask=None) -> None:
         torch = _torch()
@@ -461,6 +400,80 @@ class Plan:
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), int(bool(zero_selected)),
             _dev(grad, torch.float32, self.P, "grad"), sgd, _dev(w, torch.float32, self.P, "w"),
             _dev(v, torch.float32, self.P, "v"), _stream_ptr()))
+
+
+class DeferredResidual:
+    """Buffer rotation of the deferred-residual step (host bookkeeping only).
+
+    Keeps `depth` earlier gradient batches: the norm pass stores a every
+    depth+1 steps, the other steps re-form the residual from the held layer
+    tables and masks.  The caller passes each step's layer table and keeps its
+    tensors unchanged while they are in the history (the next `depth` steps).
+    The residual starts at zero, described by an all-ones mask (every chunk
+    "sent" before the first step), so the buffer is not read until written.
+    depth = 0 is the lazy-zero form."""
+
+    def __init__(self, plan: Plan, depth: int, resid=None):
+        torch = _torch()
+        if depth < 0 or depth > MAX_AGE:
+            raise ValueError("depth must be in [0, %d]" % MAX_AGE)
+        self.plan, self.depth = plan, depth
+        W, mw = plan.W, plan.mask_words
+        self.resid = plan.empty_residual() if resid is None else resid
+        self.keys = plan.empty_keys()
+        self.sel_idx = torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda")
+        self.masks = [torch.zeros((W, mw), dtype=torch.int32, device="cuda") for _ in range(depth + 2)]
+        words = []
+        for q in range(mw):
+            word = (1 << min(32, plan.n_chunks - 32 * q)) - 1
+            words.append(word - (1 << 32) if word >= (1 << 31) else word)
+        self.all_sent = torch.tensor(words, dtype=torch.int32).repeat(W, 1).cuda()
+        self.hist_masks = [self.all_sent]   # masks[j]: step t-1-j
+        self.hist_tables = []               # layer tables of steps t-1, t-2, ...
+        self.next = 0                       # mask buffer the next top-k writes
+        self.last = None                    # (hist, stored, layer_ptrs, sel) of the last step
+
+    @property
+    def age(self) -> int:
+        return len(self.hist_masks) - 1
+
+    def step(self, layer_ptrs, grad=None, w=None, v=None, lr=None, mu=None, events=None) -> bool:
+        """One step on the current stream; returns whether it stored.  events:
+        optional list of 3 torch.cuda.Event recorded after each call."""
+        p = self.plan
+        hist = p.history(self.hist_masks, self.hist_tables)
+        store = self.age >= self.depth
+        p.chunk_norm_deferred(layer_ptrs, hist, store, self.resid, self.keys)
+        if events:
+            events[0].record()
+        sel = self.masks[self.next]
+        p.chunk_topk(self.keys, self.sel_idx, sel)
+        if events:
+            events[1].record()
+        p.sparse_gather_reduce_deferred(layer_ptrs, hist, store, self.resid, sel, grad, w, v, lr, mu)
+        if events:
+            events[2].record()
+        self.last = (hist, store, layer_ptrs, sel)
+        if store:
+            self.hist_masks, self.hist_tables = [sel], []
+        else:
+            self.hist_masks = [sel] + self.hist_masks
+            self.hist_tables = [layer_ptrs] + self.hist_tables
+        self.next = (self.next + 1) % len(self.masks)
+        return store
+
+    def flush(self, out=None):
+        """Write the residual after the last step into `out` (default: the live
+        buffer, after which the history restarts at age 0 with no mask)."""
+        hist, stored, layer_ptrs, sel = self.last
+        if out is None:
+            self.plan.residual_flush(layer_ptrs, hist, stored, self.resid, sel)
+            self.hist_masks, self.hist_tables = [None], []
+            return self.resid
+        if out.data_ptr() != self.resid.data_ptr():
+            out.copy_(self.resid)
+        self.plan.residual_flush(layer_ptrs, hist, stored, out, sel)
+        return out
 
 
 class Buckets:

@@ -269,169 +269,99 @@ ga_status ga_chunk_norm_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs
         return fail(GA_ERR_ALIGN, "misaligned device buffer");
     ga_status st = check_device(p);
     if (st != GA_OK) return st;
-    return device_status(ga::launch_chunk_norm_layers(*p, d_layer_ptrs, d_residual, d_prev_mask, d_keys, stream),
-                         "chunk_norm_layers launch");
+    // the lazy-zero norm pass is the deferred one at age 0, storing
+    ga::HistArgs h;
+    memset(&h, 0, sizeof h);
+    h.layers[0] = d_layer_ptrs;
+    h.masks[0] = d_prev_mask;
+    return device_status(ga::launch_norm_hist(*p, h, true, d_residual, d_keys, stream), "chunk_norm_layers launch");
 }
 
-ga_status ga_chunk_norm_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
-                                     const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_residual || !d_prev_mask || !d_keys) return fail(GA_ERR_INVALID, "NULL argument");
-    const ga::Plan* p = as_plan(plan);
+namespace {
+
+// Validate a deferred step's history and turn it into kernel arguments.
+ga_status history_args(const ga::Plan* p, const uint64_t* d_layer_ptrs, const ga_history* hist,
+                       const uint32_t* d_sel_mask, ga::HistArgs* out) {
+    if (!hist) return fail(GA_ERR_INVALID, "history is NULL");
     if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (((uintptr_t)d_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_keys & 7u) ||
-        ((uintptr_t)d_prev_mask & 3u))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
+    if (hist->age < 0 || hist->age > GA_MAX_AGE)
+        return fail(GA_ERR_INVALID, "age %d outside [0, %d]", hist->age, GA_MAX_AGE);
+    memset(out, 0, sizeof *out);
+    out->age = hist->age;
+    out->layers[0] = d_layer_ptrs;
+    if ((uintptr_t)d_layer_ptrs & 7u) return fail(GA_ERR_ALIGN, "misaligned layer table");
+    for (int32_t j = 0; j < hist->age; ++j) {
+        const uint64_t* t = hist->d_layer_ptrs[j];
+        if (!t) return fail(GA_ERR_INVALID, "age %d needs the layer table of step t-%d", hist->age, j + 1);
+        if ((uintptr_t)t & 7u) return fail(GA_ERR_ALIGN, "misaligned layer table of step t-%d", j + 1);
+        if (t == d_layer_ptrs)
+            return fail(GA_ERR_INVALID, "the layer table of step t-%d is this step's: every step's gradients "
+                                        "must stay in their own tensors until they leave the history", j + 1);
+        for (int32_t q = 0; q < j; ++q)
+            if (t == hist->d_layer_ptrs[q])
+                return fail(GA_ERR_INVALID, "steps t-%d and t-%d share a layer table", q + 1, j + 1);
+        out->layers[j + 1] = t;
+    }
+    for (int32_t j = 0; j <= hist->age; ++j) {
+        const uint32_t* m = hist->d_masks[j];
+        if (m && ((uintptr_t)m & 3u)) return fail(GA_ERR_ALIGN, "misaligned mask of step t-%d", j + 1);
+        if (m && d_sel_mask && m == d_sel_mask)
+            return fail(GA_ERR_INVALID, "the mask of step t-%d is this step's selection buffer", j + 1);
+        out->masks[j] = m;
+    }
+    return GA_OK;
+}
+
+}  // namespace
+
+ga_status ga_chunk_norm_deferred(const ga_plan* plan, const uint64_t* d_layer_ptrs, const ga_history* hist,
+                                 int32_t store, float* d_residual, double* d_keys, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_residual || !d_keys) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    ga::HistArgs h;
+    ga_status st = history_args(p, d_layer_ptrs, hist, nullptr, &h);
     if (st != GA_OK) return st;
-    return device_status(
-        ga::launch_chunk_norm_layers_defer(*p, d_layer_ptrs, d_residual, d_prev_mask, d_keys, stream),
-        "chunk_norm_layers_defer launch");
+    if (!aligned16(d_residual) || ((uintptr_t)d_keys & 7u)) return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    st = check_device(p);
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_norm_hist(*p, h, store != 0, d_residual, d_keys, stream),
+                         "chunk_norm_deferred launch");
 }
 
-ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
-                                               const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
-                                               float* d_grad, const ga_sgd* sgd, float* d_w, float* d_v,
-                                               hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask)
-        return fail(GA_ERR_INVALID, "NULL argument");
+ga_status ga_sparse_gather_reduce_deferred(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                           const ga_history* hist, int32_t stored, const float* d_residual,
+                                           const uint32_t* d_sel_mask, float* d_grad, const ga_sgd* sgd,
+                                           float* d_w, float* d_v, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_residual || !d_sel_mask) return fail(GA_ERR_INVALID, "NULL argument");
     const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    ga::HistArgs h;
+    ga_status st = history_args(p, d_layer_ptrs, hist, d_sel_mask, &h);
+    if (st != GA_OK) return st;
     if (p->C % 256 != 0) return fail(GA_ERR_UNSUPPORTED, "chunk=%lld is not a multiple of 256", (long long)p->C);
-    if (d_prev_mask == d_sel_mask) return fail(GA_ERR_INVALID, "previous and current masks are the same buffer");
     if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
     if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
-    if (((uintptr_t)d_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_prev_mask & 3u) ||
-        ((uintptr_t)d_sel_mask & 3u) || (d_grad && !aligned16(d_grad)) ||
+    if (!aligned16(d_residual) || ((uintptr_t)d_sel_mask & 3u) || (d_grad && !aligned16(d_grad)) ||
         (sgd && (!aligned16(d_w) || !aligned16(d_v))))
         return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
+    st = check_device(p);
     if (st != GA_OK) return st;
-    return device_status(ga::launch_sparse_gather_defer(*p, d_layer_ptrs, d_residual, d_prev_mask, d_sel_mask,
-                                                        d_grad, sgd, d_w, d_v, true, stream),
-                         "sparse_gather_reduce_layers_defer launch");
+    return device_status(ga::launch_gather_hist(*p, h, stored != 0, d_residual, d_sel_mask, d_grad, sgd, d_w, d_v,
+                                                stream),
+                         "sparse_gather_reduce_deferred launch");
 }
 
-ga_status ga_chunk_norm_layers_pending(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                       const uint64_t* d_prev_layer_ptrs, float* d_residual,
-                                       const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask, double* d_keys,
-                                       hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_residual || !d_prev_mask || !d_prev2_mask || !d_keys)
-        return fail(GA_ERR_INVALID, "NULL argument");
+ga_status ga_residual_flush(const ga_plan* plan, const uint64_t* d_layer_ptrs, const ga_history* hist,
+                            int32_t stored, float* d_residual, const uint32_t* d_sel_mask, hipStream_t stream) {
+    if (!plan || !d_layer_ptrs || !d_residual || !d_sel_mask) return fail(GA_ERR_INVALID, "NULL argument");
     const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) || !aligned16(d_residual) ||
-        ((uintptr_t)d_keys & 7u) || ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
+    ga::HistArgs h;
+    ga_status st = history_args(p, d_layer_ptrs, hist, d_sel_mask, &h);
     if (st != GA_OK) return st;
-    return device_status(ga::launch_chunk_norm_layers_pending(*p, d_layer_ptrs, d_prev_layer_ptrs, d_residual,
-                                                              d_prev_mask, d_prev2_mask, d_keys, stream),
-                         "chunk_norm_layers_pending launch");
-}
-
-ga_status ga_sparse_gather_reduce_layers_pending(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                                 float* d_residual, const uint32_t* d_prev_mask,
-                                                 const uint32_t* d_sel_mask, float* d_grad, const ga_sgd* sgd,
-                                                 float* d_w, float* d_v, hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask)
-        return fail(GA_ERR_INVALID, "NULL argument");
-    const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (p->C % 256 != 0) return fail(GA_ERR_UNSUPPORTED, "chunk=%lld is not a multiple of 256", (long long)p->C);
-    if (d_prev_mask == d_sel_mask) return fail(GA_ERR_INVALID, "previous and current masks are the same buffer");
-    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
-    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
-    if (((uintptr_t)d_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_prev_mask & 3u) ||
-        ((uintptr_t)d_sel_mask & 3u) || (d_grad && !aligned16(d_grad)) ||
-        (sgd && (!aligned16(d_w) || !aligned16(d_v))))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
+    if (!aligned16(d_residual) || ((uintptr_t)d_sel_mask & 3u)) return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    st = check_device(p);
     if (st != GA_OK) return st;
-    return device_status(ga::launch_sparse_gather_defer(*p, d_layer_ptrs, d_residual, d_prev_mask, d_sel_mask,
-                                                        d_grad, sgd, d_w, d_v, false, stream),
-                         "sparse_gather_reduce_layers_pending launch");
-}
-
-ga_status ga_residual_flush_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
-                                   const uint32_t* d_prev_mask, const uint32_t* d_sel_mask, hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask)
-        return fail(GA_ERR_INVALID, "NULL argument");
-    const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (((uintptr_t)d_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_prev_mask & 3u) ||
-        ((uintptr_t)d_sel_mask & 3u))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
-    if (st != GA_OK) return st;
-    return device_status(ga::launch_residual_flush(*p, d_layer_ptrs, d_residual, d_prev_mask, d_sel_mask, stream),
-                         "residual_flush_layers launch");
-}
-
-ga_status ga_chunk_norm_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                        const uint64_t* d_prev_layer_ptrs, const uint64_t* d_prev2_layer_ptrs,
-                                        float* d_residual, const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask,
-                                        const uint32_t* d_prev3_mask, double* d_keys, hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_prev2_layer_ptrs || !d_residual || !d_prev_mask ||
-        !d_prev2_mask || !d_prev3_mask || !d_keys)
-        return fail(GA_ERR_INVALID, "NULL argument");
-    const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) ||
-        ((uintptr_t)d_prev2_layer_ptrs & 7u) || !aligned16(d_residual) || ((uintptr_t)d_keys & 7u) ||
-        ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u) || ((uintptr_t)d_prev3_mask & 3u))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
-    if (st != GA_OK) return st;
-    return device_status(ga::launch_chunk_norm_layers_pending2(*p, d_layer_ptrs, d_prev_layer_ptrs,
-                                                               d_prev2_layer_ptrs, d_residual, d_prev_mask,
-                                                               d_prev2_mask, d_prev3_mask, d_keys, stream),
-                         "chunk_norm_layers_pending2 launch");
-}
-
-ga_status ga_sparse_gather_reduce_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                                  const uint64_t* d_prev_layer_ptrs, float* d_residual,
-                                                  const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
-                                                  const uint32_t* d_prev2_mask, float* d_grad, const ga_sgd* sgd,
-                                                  float* d_w, float* d_v, hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask ||
-        !d_prev2_mask)
-        return fail(GA_ERR_INVALID, "NULL argument");
-    const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (p->C % 256 != 0) return fail(GA_ERR_UNSUPPORTED, "chunk=%lld is not a multiple of 256", (long long)p->C);
-    if (d_prev_mask == d_sel_mask || d_prev2_mask == d_sel_mask)
-        return fail(GA_ERR_INVALID, "an earlier mask and the current mask are the same buffer");
-    if (!d_grad && !sgd) return fail(GA_ERR_INVALID, "neither a gradient output nor an SGD update requested");
-    if (sgd && (!d_w || !d_v)) return fail(GA_ERR_INVALID, "SGD update needs w and v");
-    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) || !aligned16(d_residual) ||
-        ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_sel_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u) ||
-        (d_grad && !aligned16(d_grad)) || (sgd && (!aligned16(d_w) || !aligned16(d_v))))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
-    if (st != GA_OK) return st;
-    return device_status(ga::launch_sparse_gather_pending2(*p, d_layer_ptrs, d_prev_layer_ptrs, d_residual,
-                                                           d_prev_mask, d_sel_mask, d_prev2_mask, d_grad, sgd, d_w,
-                                                           d_v, stream),
-                         "sparse_gather_reduce_layers_pending2 launch");
-}
-
-ga_status ga_residual_flush_layers2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                    const uint64_t* d_prev_layer_ptrs, float* d_residual,
-                                    const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
-                                    const uint32_t* d_prev2_mask, hipStream_t stream) {
-    if (!plan || !d_layer_ptrs || !d_prev_layer_ptrs || !d_residual || !d_prev_mask || !d_sel_mask ||
-        !d_prev2_mask)
-        return fail(GA_ERR_INVALID, "NULL argument");
-    const ga::Plan* p = as_plan(plan);
-    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
-    if (((uintptr_t)d_layer_ptrs & 7u) || ((uintptr_t)d_prev_layer_ptrs & 7u) || !aligned16(d_residual) ||
-        ((uintptr_t)d_prev_mask & 3u) || ((uintptr_t)d_sel_mask & 3u) || ((uintptr_t)d_prev2_mask & 3u))
-        return fail(GA_ERR_ALIGN, "misaligned device buffer");
-    ga_status st = check_device(p);
-    if (st != GA_OK) return st;
-    return device_status(ga::launch_residual_flush(*p, d_layer_ptrs, d_residual, d_prev_mask, d_sel_mask, stream,
-                                                   d_prev_layer_ptrs, d_prev2_mask),
-                         "residual_flush_layers2 launch");
+    return device_status(ga::launch_flush_hist(*p, h, stored != 0, d_residual, d_sel_mask, stream),
+                         "residual_flush launch");
 }
 
 ga_status ga_reduce_variant(const ga_plan* plan, const void* d_bucket, ga_order order, int32_t wire_fp16, float* d_grad,

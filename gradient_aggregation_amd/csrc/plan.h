@@ -40,48 +40,24 @@ hipError_t launch_tree_scaled(const Plan& p, const void* bucket, float scale, fl
                               float* w, float* v, hipStream_t s);
 hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid,
                              const uint32_t* prev_mask, double* keys, hipStream_t s);
-hipError_t launch_chunk_norm_layers(const Plan& p, const uint64_t* layer_ptrs, float* resid,
-                                    const uint32_t* prev_mask, double* keys, hipStream_t s);
-// launch_chunk_norm_layers in deferred mode (prev_mask required): a chunk
-// sent in the previous step does not store its a.
-hipError_t launch_chunk_norm_layers_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
-                                          const uint32_t* prev_mask, double* keys, hipStream_t s);
-// launch_chunk_norm_layers_defer, and a chunk set in prev2_mask but not in
-// prev_mask takes the previous step's gradient (prev_layer_ptrs) + 0 as its
-// residual.
-hipError_t launch_chunk_norm_layers_pending(const Plan& p, const uint64_t* layer_ptrs,
-                                            const uint64_t* prev_layer_ptrs, float* resid,
-                                            const uint32_t* prev_mask, const uint32_t* prev2_mask, double* keys,
-                                            hipStream_t s);
-// Gather-reduce for deferred mode: a chunk sent now and in the previous step
-// is read from the gradient tensors; with materialize, one sent before but not
-// now gets its residual (the widened gradient) written.  C must be a multiple
-// of 256.
-hipError_t launch_sparse_gather_defer(const Plan& p, const uint64_t* layer_ptrs, float* resid,
-                                      const uint32_t* prev_mask, const uint32_t* sel_mask, float* grad,
-                                      const ga_sgd* sgd, float* w, float* v, bool materialize, hipStream_t s);
-// The residual of every chunk set in prev_mask but not in sel_mask becomes
-// the widened gradient (layer_ptrs) + 0; with prev2_mask (depth 2), that of
-// every chunk set in prev2_mask and in neither later mask becomes g0 + (g1 +
-// 0), g1 from prev_layer_ptrs.
-hipError_t launch_residual_flush(const Plan& p, const uint64_t* layer_ptrs, float* resid, const uint32_t* prev_mask,
-                                 const uint32_t* sel_mask, hipStream_t s, const uint64_t* prev_layer_ptrs = nullptr,
-                                 const uint32_t* prev2_mask = nullptr);
-// Depth-2 pending form of the norm pass: launch_chunk_norm_layers_pending,
-// except that a chunk pending one step does not store its a, and a chunk set
-// in prev3_mask and in neither later mask takes g1 + (g2 + 0) as its
-// residual (prev_layer_ptrs, prev2_layer_ptrs).
-hipError_t launch_chunk_norm_layers_pending2(const Plan& p, const uint64_t* layer_ptrs,
-                                             const uint64_t* prev_layer_ptrs, const uint64_t* prev2_layer_ptrs,
-                                             float* resid, const uint32_t* prev_mask, const uint32_t* prev2_mask,
-                                             const uint32_t* prev3_mask, double* keys, hipStream_t s);
-// Depth-2 pending gather: as launch_sparse_gather_defer without
-// materialization, and a chunk sent now, set in prev2_mask and not in
-// prev_mask has the leaf g0 + (g1 + 0), g1 from prev_layer_ptrs.
-hipError_t launch_sparse_gather_pending2(const Plan& p, const uint64_t* layer_ptrs, const uint64_t* prev_layer_ptrs,
-                                         float* resid, const uint32_t* prev_mask, const uint32_t* sel_mask,
-                                         const uint32_t* prev2_mask, float* grad, const ga_sgd* sgd, float* w,
-                                         float* v, hipStream_t s);
+// The deferred-residual form (history.hip).  layers[0] is this step's layer
+// table and layers[j] that of step t-j (j <= age); masks[j] the selection of
+// step t-1-j (j <= age), or nullptr.
+struct HistArgs {
+    const uint64_t* layers[GA_MAX_AGE + 1];
+    const uint32_t* masks[GA_MAX_AGE + 1];
+    int32_t age;
+};
+// Norm pass: keys of a_t; with store, a_t written into resid.
+hipError_t launch_norm_hist(const Plan& p, const HistArgs& h, bool store, float* resid, double* keys,
+                            hipStream_t s);
+// Gather-reduce of the chunks set in sel (stored: this step's norm pass stored).
+hipError_t launch_gather_hist(const Plan& p, const HistArgs& h, bool stored, const float* resid,
+                              const uint32_t* sel, float* grad, const ga_sgd* sgd, float* w, float* v,
+                              hipStream_t s);
+// The residual after the step: +0 on the chunks set in sel, a_t elsewhere.
+hipError_t launch_flush_hist(const Plan& p, const HistArgs& h, bool stored, float* resid, const uint32_t* sel,
+                             hipStream_t s);
 hipError_t launch_tree_layers(const Plan& p, const uint64_t* layer_ptrs, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
 // launch_tree_layers over a sub-list of layers: worker w's layer l is entry

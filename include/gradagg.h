@@ -47,8 +47,10 @@
  * exception crosses this interface.
  *
  * Determinism.  Every result is a fixed function of the inputs: the summation
- * order is the fixed tree below, no atomics are used, and repeated calls give
- * bitwise identical outputs [FC FAQ].
+ * order is the fixed tree below, no floating-point value is accumulated by
+ * atomics (the only atomics are integer increments of the top-k's histogram
+ * counters in LDS, whose totals do not depend on their order), and repeated
+ * calls give bitwise identical outputs [FC FAQ].
  */
 #ifndef GRADAGG_H
 #define GRADAGG_H
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GA_ABI_VERSION 1
+#define GA_ABI_VERSION 2
 #define GA_MAX_WORKERS 1024
 #define GA_MAX_CHUNKS 65536
 /* Most elements per worker (P) of a plan or an SGD call: every 1-D grid of
@@ -254,152 +256,91 @@ ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const 
                                   float* d_w, float* d_v, hipStream_t stream);
 
 /*
- * Coarse-grained sparse communication [GF] in deferred-residual form, for
- * gradients held as per-layer tensors (a lazy-zero mode that moves fewer
- * bytes).  A chunk a worker sent in the previous step has a zero residual, so
- * its a is the worker's widened gradient; the norm pass does not store it and
- * the gather reads the gradient instead.  One step is
- *   ga_chunk_norm_layers_defer(prev) -> ga_chunk_topk(cur) ->
- *   ga_sparse_gather_reduce_layers_defer(prev, cur)
- * with two mask buffers that swap roles every step (the first step passes an
- * all-zero prev).  Keys, selection, mean gradient, w and v are those of the
- * lazy-zero sequence of ga_chunk_norm_layers / ga_sparse_gather_reduce, bit
- * for bit, and after the gather d_residual holds what that sequence leaves:
- * the new residual, with the chunks sent now read as zero (pass cur as the
- * next step's prev).
+ * Coarse-grained sparse communication [GF] with a deferred residual, for
+ * gradients held as per-layer tensors: the same step as ga_chunk_norm_layers
+ * -> ga_chunk_topk -> ga_sparse_gather_reduce, moving fewer bytes.
  *
- * ga_chunk_norm_layers_defer: as ga_chunk_norm_layers with d_prev_mask
- *   required; for a chunk set in d_prev_mask, a is not stored (d_residual keeps
- *   stale values there).
- */
-ga_status ga_chunk_norm_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
-                                     const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream);
-
-/*
- * ga_sparse_gather_reduce_layers_defer: the gather-reduce of the step, with
- * the step's gradient tensors (d_layer_ptrs, as in ga_chunk_norm_layers):
- *   leaf of worker w, chunk c sent now (d_sel_mask) = widened gradient + 0
- *     if c was also sent in the previous step (d_prev_mask), else d_residual;
- *   a chunk set in d_prev_mask but not in d_sel_mask gets d_residual = the
- *     widened gradient + 0 (its residual after this step);
- *   then the tree, mean and SGD of ga_sparse_gather_reduce.
- * d_prev_mask and d_sel_mask must be different buffers; the chunk size must be
- * a multiple of 256 elements (GA_ERR_UNSUPPORTED otherwise).  d_grad, sgd,
- * d_w, d_v: as in ga_tree_reduce.
- */
-ga_status ga_sparse_gather_reduce_layers_defer(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
-                                               const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
-                                               float* d_grad, const ga_sgd* sgd, float* d_w, float* d_v,
-                                               hipStream_t stream);
-
-/*
- * Pending-residual form of the deferred step [GF]: the residual of a chunk a
- * worker sent in step t-1 but not in step t is, after step t, that worker's
- * widened step-t gradient + 0 (a was the gradient plus a zero residual).  It
- * is not written at step t: the norm pass of step t+1 reads it from the
- * step-t gradient tensors (2 B per binary16 element instead of a 4 B write
- * and a 4 B read).  The caller therefore keeps each step's gradient tensors,
- * unchanged, until the next step's norm pass has run (for example, two
- * gradient buffers per worker used in turn).  One step t is
- *   ga_chunk_norm_layers_pending(cur layers, prev layers, prev, prev2) ->
- *   ga_chunk_topk(into prev2's buffer) ->
- *   ga_sparse_gather_reduce_layers_pending(cur layers, prev, cur)
- * with the same two mask buffers as the deferred form: prev holds step t-1's
- * mask and the other buffer still holds step t-2's when the norm pass reads
- * it as prev2, before the top-k overwrites it with step t's.  The first step
- * passes all-zero masks (and any valid layer table as prev layers).  Keys,
- * selection, mean gradient, w and v are those of the lazy-zero sequence, bit
- * for bit.
+ * The residual recurrence is a_t = leaf_t + r_{t-1} (r_0 = 0), and r_t = +0 on
+ * the chunks a worker sends at step t, a_t elsewhere.  d_residual (R, [W][ld]
+ * binary32) is written only by a norm pass the caller marks as storing (it
+ * writes a_t of every chunk) and by ga_residual_flush (it writes r_t).  Between
+ * two writes the residual is re-formed from what the caller still holds,
+ * described by a ga_history at step t:
+ *   age            R was last written by step t-1-age's storing norm pass or
+ *                  flush (0 <= age <= GA_MAX_AGE); a zero-filled R counts as
+ *                  written at step 0;
+ *   d_masks[j]     j = 0..age: the selection mask of step t-1-j ([W][mw], as
+ *                  written by ga_chunk_topk), or NULL if no chunk counts as
+ *                  sent then (steps before the first, or the step a flush ended);
+ *   d_layer_ptrs[j] j = 0..age-1: the layer table of step t-1-j (as
+ *                  d_layer_ptrs of ga_tree_reduce_layers); those tensors must
+ *                  still hold that step's gradients.
+ * For worker w and chunk c, let j be the smallest index whose mask has c set
+ * for w: then r_{t-1} = g_{t-1} + (g_{t-2} + (... + (g_{t-j} + +0))), the j
+ * gradients since that step added onto +0 (r_{t-1} = +0 for j = 0); if no mask
+ * has it set, r_{t-1} = g_{t-1} + (... + (g_{t-age} + R)).  Every g is the
+ * exact widening of the worker's gradient, and the adds are the recurrence's
+ * own, in its order, so every value equals the plain recurrence bit for bit.
  *
- * ga_chunk_norm_layers_pending: as ga_chunk_norm_layers_defer, and a chunk set
- *   in d_prev2_mask but not in d_prev_mask takes d_prev_layer_ptrs' widened
- *   gradient + 0 as its residual (d_residual is not read there); a is stored.
- *   d_prev_layer_ptrs: [W*L] device addresses of the previous step's tensors,
- *   laid out as d_layer_ptrs.  Errors as ga_chunk_norm_layers_defer.
+ * One step t:
+ *   ga_chunk_norm_deferred(g_t, hist, store)   keys; R <- a_t if store
+ *   ga_chunk_topk(keys) -> m_t
+ *   ga_sparse_gather_reduce_deferred(g_t, hist, store, m_t)
+ * then the next step's history is {age 0, masks {m_t}} if this step stored,
+ * else {age + 1, masks {m_t, the old masks}, tables {g_t, the old tables}}.
+ * A caller that keeps D earlier gradient batches stores every D+1 steps (D = 0:
+ * every step, which is the lazy-zero form; the mask buffers then rotate over
+ * D+2 buffers).  A zero residual can be described without reading R: age 0
+ * and d_masks[0] = a mask of all ones (every chunk "sent" before step 1).
+ * Keys, selection, mean gradient, w and v equal the plain recurrence (and the
+ * oracle) bit for bit.
  */
-ga_status ga_chunk_norm_layers_pending(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                       const uint64_t* d_prev_layer_ptrs, float* d_residual,
-                                       const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask, double* d_keys,
-                                       hipStream_t stream);
+#define GA_MAX_AGE 2
+
+typedef struct {
+    int32_t age;
+    const uint32_t* d_masks[GA_MAX_AGE + 1];
+    const uint64_t* d_layer_ptrs[GA_MAX_AGE];
+} ga_history;
 
 /*
- * ga_sparse_gather_reduce_layers_pending: ga_sparse_gather_reduce_layers_defer
- * without the residual write of the chunks set in d_prev_mask but not in
- * d_sel_mask.  Afterwards d_residual holds the new residual except on those
- * chunks, whose residual is the widened gradient of d_layer_ptrs + 0 (written
- * by the next ga_chunk_norm_layers_pending, or by ga_residual_flush_layers).
- * Arguments and errors as ga_sparse_gather_reduce_layers_defer.
+ * The norm pass of a deferred step: for every worker and chunk, a_t = g_t +
+ * r_{t-1} (r_{t-1} re-formed as above), its key as in ga_chunk_norm, and with
+ * store != 0, d_residual <- a_t on every chunk.  d_layer_ptrs: this step's
+ * layer table.  Errors: GA_ERR_INVALID (NULL argument, dense-only plan, age
+ * outside [0, GA_MAX_AGE], a missing earlier table, an earlier table pointer
+ * equal to this step's or to another earlier one: the tensors of different
+ * steps must be different buffers), GA_ERR_ALIGN, GA_ERR_DEVICE.
  */
-ga_status ga_sparse_gather_reduce_layers_pending(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                                 float* d_residual, const uint32_t* d_prev_mask,
-                                                 const uint32_t* d_sel_mask, float* d_grad, const ga_sgd* sgd,
-                                                 float* d_w, float* d_v, hipStream_t stream);
+ga_status ga_chunk_norm_deferred(const ga_plan* plan, const uint64_t* d_layer_ptrs, const ga_history* hist,
+                                 int32_t store, float* d_residual, double* d_keys, hipStream_t stream);
 
 /*
- * ga_residual_flush_layers: writes the pending residuals of a step, so that
- * d_residual holds the whole residual (before a checkpoint, at the end of
- * training, or before the step's gradient tensors are reused): for every
- * chunk set in d_prev_mask but not in d_sel_mask, d_residual = the widened
- * gradient of d_layer_ptrs + 0.  Pass the step's layer table and its two
- * masks, as given to ga_sparse_gather_reduce_layers_pending.  Writing them is
- * harmless to the next pending step, which computes the same values itself.
- * Errors: GA_ERR_INVALID (NULL, dense-only plan), GA_ERR_ALIGN, GA_ERR_DEVICE.
+ * The gather-reduce of a deferred step: worker w sends a_t on the chunks set
+ * in d_sel_mask (read from d_residual if this step's norm pass stored, else
+ * re-formed from the history as the norm pass formed it); absent values enter
+ * the fixed tree as +0; g = S * fl32(1/W); d_grad, sgd, d_w, d_v as in
+ * ga_tree_reduce.  d_residual is only read.  hist and stored: as given to
+ * this step's norm pass.  d_sel_mask must differ from every history mask
+ * (GA_ERR_INVALID); the chunk size must be a multiple of 256 elements
+ * (GA_ERR_UNSUPPORTED).  Other errors as ga_chunk_norm_deferred.
  */
-ga_status ga_residual_flush_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
-                                   const uint32_t* d_prev_mask, const uint32_t* d_sel_mask, hipStream_t stream);
+ga_status ga_sparse_gather_reduce_deferred(const ga_plan* plan, const uint64_t* d_layer_ptrs,
+                                           const ga_history* hist, int32_t stored, const float* d_residual,
+                                           const uint32_t* d_sel_mask, float* d_grad, const ga_sgd* sgd,
+                                           float* d_w, float* d_v, hipStream_t stream);
 
 /*
- * Depth-2 pending form [GF]: as the pending form, and a chunk pending at step
- * t (sent in step t-2, not in step t-1) does not store its a either: that a
- * is g_t + (g_{t-1} + 0), recomputed from the two gradients by the gather
- * (if the chunk is sent now), by the next norm pass (if not), or by
- * ga_residual_flush_layers2.  The caller keeps the gradient tensors of the
- * previous two steps, unchanged, and three mask buffers used in turn: the
- * buffer the top-k of step t writes holds step t-3's mask, which the norm
- * pass reads first.  One step t is
- *   ga_chunk_norm_layers_pending2(g_t, g_{t-1}, g_{t-2}, m_{t-1}, m_{t-2}, m_{t-3}) ->
- *   ga_chunk_topk(into m_{t-3}'s buffer: m_t) ->
- *   ga_sparse_gather_reduce_layers_pending2(g_t, g_{t-1}, m_{t-1}, m_t, m_{t-2})
- * with all-zero masks (and any valid layer tables) for the steps before the
- * first.  Keys, selection, mean gradient, w and v are those of the lazy-zero
- * sequence, bit for bit.
- *
- * ga_chunk_norm_layers_pending2: as ga_chunk_norm_layers_pending with
- *   d_prev_mask = m_{t-1}, d_prev2_mask = m_{t-2}, except that the a of a
- *   chunk set in d_prev2_mask but not in d_prev_mask is not stored; and a
- *   chunk set in d_prev3_mask (m_{t-3}) and in neither later mask takes
- *   g_{t-1} + (g_{t-2} + 0) as its residual (d_residual is not read there;
- *   d_prev2_layer_ptrs: the tensors of step t-2); its a is stored.
+ * Write the residual after a deferred step into d_residual: r_t = +0 on the
+ * chunks set in d_sel_mask, a_t elsewhere (already there if the step stored,
+ * else re-formed from the history).  Arguments as given to the step's gather.
+ * Afterwards d_residual is the whole residual (for a checkpoint, or before the
+ * gradient tensors are reused), and the next step passes age 0 with
+ * d_masks[0] = NULL: no earlier tensor or mask is needed to resume.
+ * Errors as ga_sparse_gather_reduce_deferred (no chunk-size limit).
  */
-ga_status ga_chunk_norm_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                        const uint64_t* d_prev_layer_ptrs, const uint64_t* d_prev2_layer_ptrs,
-                                        float* d_residual, const uint32_t* d_prev_mask, const uint32_t* d_prev2_mask,
-                                        const uint32_t* d_prev3_mask, double* d_keys, hipStream_t stream);
-
-/*
- * ga_sparse_gather_reduce_layers_pending2: ga_sparse_gather_reduce_layers_pending,
- * and the leaf of a chunk sent now (d_sel_mask), set in d_prev2_mask and not
- * in d_prev_mask is g_t + (g_{t-1} + 0), read from d_layer_ptrs and
- * d_prev_layer_ptrs.  d_sel_mask must differ from both earlier masks
- * (GA_ERR_INVALID); otherwise as ga_sparse_gather_reduce_layers_pending.
- */
-ga_status ga_sparse_gather_reduce_layers_pending2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                                  const uint64_t* d_prev_layer_ptrs, float* d_residual,
-                                                  const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
-                                                  const uint32_t* d_prev2_mask, float* d_grad, const ga_sgd* sgd,
-                                                  float* d_w, float* d_v, hipStream_t stream);
-
-/*
- * ga_residual_flush_layers2: writes the pending residuals of a depth-2 step
- * (arguments as given to its gather): chunks set in d_prev_mask but not in
- * d_sel_mask get g_t + 0; chunks set in d_prev2_mask and in neither later
- * mask get g_t + (g_{t-1} + 0).  Afterwards d_residual holds the whole
- * residual.  Harmless to later steps.  Errors as ga_residual_flush_layers.
- */
-ga_status ga_residual_flush_layers2(const ga_plan* plan, const uint64_t* d_layer_ptrs,
-                                    const uint64_t* d_prev_layer_ptrs, float* d_residual,
-                                    const uint32_t* d_prev_mask, const uint32_t* d_sel_mask,
-                                    const uint32_t* d_prev2_mask, hipStream_t stream);
+ga_status ga_residual_flush(const ga_plan* plan, const uint64_t* d_layer_ptrs, const ga_history* hist,
+                            int32_t stored, float* d_residual, const uint32_t* d_sel_mask, hipStream_t stream);
 
 /*
  * Momentum SGD on binary32 master weights, Caffe form (FireCaffe runs Caffe

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(ga):
     lib = ctypes.CDLL(ga.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
-    assert ga.lib().ga_abi_version() == 1
+    assert ga.lib().ga_abi_version() == 2
 
 
 def test_status_strings(ga):
@@ -89,16 +89,12 @@ def test_calls_reject_null_plan_without_launching(ga):
     assert L.ga_chunk_topk(None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_sparse_gather_reduce(None, None, None, 1, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_bucket_pack(None, None, None, None) == ga.GA_ERR_INVALID
-    assert L.ga_chunk_norm_layers_defer(None, None, None, None, None, None) == ga.GA_ERR_INVALID
-    assert L.ga_sparse_gather_reduce_layers_defer(None, None, None, None, None, None, None, None, None,
-                                                  None) == ga.GA_ERR_INVALID
-    assert L.ga_chunk_norm_layers_pending(None, None, None, None, None, None, None, None) == ga.GA_ERR_INVALID
-    assert L.ga_sparse_gather_reduce_layers_pending(None, None, None, None, None, None, None, None, None,
-                                                    None) == ga.GA_ERR_INVALID
-    assert L.ga_residual_flush_layers(None, None, None, None, None, None) == ga.GA_ERR_INVALID
-    assert L.ga_chunk_norm_layers_pending2(*([None] * 10)) == ga.GA_ERR_INVALID
-    assert L.ga_sparse_gather_reduce_layers_pending2(*([None] * 12)) == ga.GA_ERR_INVALID
-    assert L.ga_residual_flush_layers2(*([None] * 8)) == ga.GA_ERR_INVALID
+    h = ga.History()
+    assert L.ga_chunk_norm_deferred(None, None, None, 0, None, None, None) == ga.GA_ERR_INVALID
+    assert L.ga_sparse_gather_reduce_deferred(None, None, None, 0, None, None, None, None, None, None,
+                                              None) == ga.GA_ERR_INVALID
+    assert L.ga_residual_flush(None, None, None, 0, None, None, None) == ga.GA_ERR_INVALID
+    assert L.ga_chunk_norm_deferred(None, 8, ctypes.byref(h), 0, 16, 8, None) == ga.GA_ERR_INVALID
     assert L.ga_reduce_variant(None, None, 0, 0, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_tree_reduce_layers(None, None, None, None, None, None, None) == ga.GA_ERR_INVALID
     assert L.ga_chunk_norm_layers(None, None, None, None, None, None) == ga.GA_ERR_INVALID
@@ -108,6 +104,16 @@ def test_calls_reject_null_plan_without_launching(ga):
     s = ga.SGD(0.01, 0.9)
     assert L.ga_sgd_momentum_apply(0, None, None, None, ctypes.byref(s), None) == ga.GA_OK
     assert L.ga_sgd_momentum_apply(16, 8, 16, 32, ctypes.byref(s), None) == ga.GA_ERR_ALIGN
+
+
+def test_history_struct_matches_header(ga):
+    """The binding's ga_history has the header's layout (age, GA_MAX_AGE + 1
+    mask pointers, GA_MAX_AGE layer-table pointers)."""
+    src = open(HEADER).read()
+    m = re.search(r"#define GA_MAX_AGE (\d+)", src)
+    assert m and int(m.group(1)) == ga.MAX_AGE
+    assert ctypes.sizeof(ga.History) == 8 + 8 * (2 * ga.MAX_AGE + 1)
+    assert ga.History.d_masks.offset == 8 and ga.History.d_layer_ptrs.offset == 8 + 8 * (ga.MAX_AGE + 1)
 
 
 def test_product_path_has_no_cpu_fallback(ga):

@@ -1,5 +1,5 @@
 """Host-side checks of bench.py's helpers (no GPU): the one-GPU refusal, the
-byte counts of a deferred step from its two masks, and the rule that counter
+selection counts of a step from its masks, and the rule that counter
 traffic is reported only for the kernel sources it was measured on."""
 import json
 import os
@@ -33,9 +33,9 @@ def _mask(bits, W, n_c):
     return torch.from_numpy(m.view(np.int32))
 
 
-def test_deferred_bytes_brute_force():
-    """Counts and bytes against a direct loop over (worker, chunk), with a
-    ragged last chunk and chunks past bit 31 of a word."""
+def test_selection_stats_brute_force():
+    """Counts against a direct loop over (worker, chunk), with chunks past bit
+    31 of a word."""
     rng = np.random.default_rng(5)
     W, C, n_c = 3, 256, 70
     P = (n_c - 1) * C + 77
@@ -44,19 +44,12 @@ def test_deferred_bytes_brute_force():
     cur = {(w, c) for w in range(W) for c in range(n_c) if rng.random() < 0.3}
     prev |= {(0, n_c - 1)}
     cur |= {(0, n_c - 1), (1, n_c - 1)}
-    got = bench.deferred_bytes(plan, _mask(prev, W, n_c), _mask(cur, W, n_c), P, 2)
-
-    def length(c):
-        return C if c < n_c - 1 else P - (n_c - 1) * C
-
-    resent = prev & cur
-    new = cur - prev
-    mat = prev - cur
-    assert got["chunks_resent"] == len(resent)
-    assert got["chunks_new"] == len(new)
-    assert got["chunks_materialized"] == len(mat)
-    assert got["gather_bytes"] == sum(length(c) for _, c in resent) * 2 + sum(length(c) for _, c in new) * 4 + 16 * P
-    assert got["materialize_bytes"] == sum(length(c) for _, c in mat) * 6
+    got = bench.selection_stats(plan, _mask(prev, W, n_c), _mask(cur, W, n_c), P)
+    assert got["pairs_sent"] == len(cur)
+    assert got["pairs_sent_again"] == len(prev & cur)
+    assert got["pairs_newly_sent"] == len(cur - prev)
+    assert got["chunks_sent_by_any_worker"] == len({c for _, c in cur})
+    assert bench.selection_stats(plan, None, _mask(cur, W, n_c), P)["pairs_newly_sent"] == len(cur)
 
 
 def test_traffic_needs_the_profiled_sources(tmp_path):
@@ -79,7 +72,8 @@ def test_traffic_needs_the_profiled_sources(tmp_path):
     assert bench.measured_traffic(str(tmp_path / "absent.json"), "k_x") is None
 
 
-@pytest.mark.parametrize("name", ["alexnet128_sparse", "googlenet", "alexnet16", "nin"])
+@pytest.mark.parametrize("name", sorted(f[len("traffic_"):-len(".json")] for f in os.listdir(os.path.join(ROOT, "profiles"))
+                                         if f.startswith("traffic_") and f.endswith(".json")))
 def test_committed_traffic_matches_current_sources(name):
     """Every committed counter record still describes the kernel sources in
     the tree, so bench.py reports its traffic."""

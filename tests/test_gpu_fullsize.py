@@ -3,11 +3,14 @@ benchmark times, against the oracle run on the host cores.
 
 NiN-, GoogLeNet- and AlexNet-shaped dense aggregation are compared on every
 element, from a packed bucket and from the per-layer tensors.  The
-AlexNet-shaped W=128 sparse workload is run as benchmarked (2048 per-layer
-tensors read with zero copy, 3 consecutive steps, lazy-zero residual with one
-reused mask buffer) and compared on every selected index, every key, every
-mean-gradient/weight/velocity element and the residual of a sample of
-workers."""
+AlexNet-shaped W=128 sparse workload (2048 per-layer tensors read with zero
+copy) is run in the lazy-zero sequence of the boundary's calls and in the
+benchmarked deferred form, over consecutive steps, and compared on every
+selected index, every key and every element of the mean gradient, the
+weights, the velocity and the residual of all 128 workers.  The deferred form
+is also checkpointed (flushed, saved to the host) and resumed from the saved
+state alone, and one of its steps is repeated from the same state to show it
+bitwise deterministic."""
 import os
 import time
 
@@ -67,7 +70,28 @@ def test_dense_full_size(ga, name, source):
         log("%s (%s) step %d ok in %.1fs" % (name, source, step, time.time() - t0))
 
 
+def sent_elements(mask, C, P):
+    """[W][P] bool: the elements of the chunks set in a [W][mw] mask."""
+    m = np.asarray(mask).view(np.uint32).astype(np.int64)
+    n_c = (P + C - 1) // C
+    ch = np.arange(n_c)
+    return np.repeat(((m[:, ch >> 5] >> (ch & 31)) & 1).astype(bool), C, axis=1)[:, :P]
+
+
+def assert_residual(got, r_ref, P, name, lazy_mask=None, C=0):
+    """Every worker's residual, worker by worker; with lazy_mask, the chunks it
+    sets are read as zero (the lazy-zero buffer)."""
+    for w in range(got.shape[0]):
+        r = host(got[w, :P])
+        if lazy_mask is not None:
+            r = r.copy()
+            r[sent_elements(lazy_mask[w:w + 1], C, P)[0]] = 0.0
+        assert_same_bits(r, r_ref[w, :P], "%s, worker %d" % (name, w))
+
+
 def test_sparse_alexnet128_full_size(ga):
+    """The lazy-zero sequence of the boundary's calls: chunk_norm_layers ->
+    chunk_topk -> sparse_gather_reduce without zeroing, one mask buffer."""
     wl = workloads.WORKLOADS["alexnet128_sparse"]
     C = wl.chunk
     plan = ga.Plan(wl.W, wl.numels, True, chunk=C, keep_ratio=wl.rho)
@@ -83,7 +107,6 @@ def test_sparse_alexnet128_full_size(ga):
     idx = torch.empty((wl.W, k), dtype=torch.int32, device="cuda")
     mask = torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda")
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
-    sample = [0, 1, 63, 127]
     for step in (1, 2, 3):
         t0 = time.time()
         b = workloads.grad_bucket(wl, step, ld, seg=seg)
@@ -94,7 +117,6 @@ def test_sparse_alexnet128_full_size(ga):
         res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         del b
         log("step %d oracle in %.1fs" % (step, time.time() - t1))
-        # lazy-zero mode, one mask buffer reused across steps, as benchmarked
         plan.chunk_norm_layers(ptrs, rd, keys, mask if step > 1 else None)
         plan.chunk_topk(keys, idx, mask)
         plan.sparse_gather_reduce(rd, mask, False, gd, wd, vd, wl.lr, wl.mu)
@@ -108,13 +130,7 @@ def test_sparse_alexnet128_full_size(ga):
         assert_close(host(gd), res.gbar, TOL_FP32, "gbar")
         assert_same_bits(host(wd), w_ref, "w")
         assert_same_bits(host(vd), v_ref, "v")
-        m = host(mask).view(np.uint32)
-        for w in sample:
-            r = host(rd[w, :P]).copy()
-            for c in range(n_c):
-                if (int(m[w, c >> 5]) >> (c & 31)) & 1:
-                    r[c * C:min((c + 1) * C, P)] = 0.0
-            assert_same_bits(r, r_ref[w, :P], "residual of worker %d" % w)
+        assert_residual(rd, r_ref, P, "lazy residual step %d" % step, lazy_mask=host(mask), C=C)
         log("step %d compared in %.1fs (total %.1fs)" % (step, time.time() - t1, time.time() - t0))
 
 
@@ -148,74 +164,124 @@ def test_buckets_alexnet16_full_size(ga, cap):
         log("alexnet16 buckets (cap %d) step %d ok in %.1fs" % (cap, step, time.time() - t0))
 
 
-@pytest.mark.parametrize("mode,steps", [("defer", 3), ("pending", 4), ("pending2", 5)])
-def test_sparse_alexnet128_full_size_deferred(ga, mode, steps):
-    """The AlexNet-shaped W=128 sparse workload as benchmarked: 2048 per-layer
-    tensors, consecutive steps in deferred lazy-zero mode (two mask buffers)
-    or its pending forms (the previous steps' tensors kept; the residual is
-    compared through a flushed copy), every output compared with the oracle."""
+class DeviceRun:
+    """One GPU instance of the deferred step: its residual, state and history."""
+
+    def __init__(self, plan, w_init):
+        self.plan = plan
+        self.rd = plan.empty_residual()
+        self.keys = plan.empty_keys()
+        self.idx = torch.empty((plan.W, plan.k), dtype=torch.int32, device="cuda")
+        self.wd, self.vd = to_dev(w_init.copy()), torch.zeros(plan.P, dtype=torch.float32, device="cuda")
+        self.gd = torch.empty(plan.P, dtype=torch.float32, device="cuda")
+        self.masks, self.tables = [None], []
+        self.last = None
+
+    def step(self, ptrs, depth, lr, mu):
+        p = self.plan
+        store = len(self.masks) - 1 >= depth
+        hist = p.history(self.masks, self.tables)
+        sel = torch.zeros((p.W, p.mask_words), dtype=torch.int32, device="cuda")
+        p.chunk_norm_deferred(ptrs, hist, store, self.rd, self.keys)
+        p.chunk_topk(self.keys, self.idx, sel)
+        p.sparse_gather_reduce_deferred(ptrs, hist, store, self.rd, sel, self.gd, self.wd, self.vd, lr, mu)
+        self.last = (ptrs, hist, store, sel)
+        if store:
+            self.masks, self.tables = [sel], []
+        else:
+            self.masks, self.tables = [sel] + self.masks, [ptrs] + self.tables
+
+    def flush(self, out):
+        ptrs, hist, store, sel = self.last
+        if out.data_ptr() != self.rd.data_ptr():
+            out.copy_(self.rd)
+        self.plan.residual_flush(ptrs, hist, store, out, sel)
+        return out
+
+    def check(self, res, w_ref, v_ref, r_ref, scratch, name):
+        assert np.array_equal(host(self.idx), res.sel_idx), name + ": selected chunk indices differ"
+        assert np.array_equal(host(self.masks[0]).view(np.uint32), res.sel_mask), name + ": mask"
+        assert_close(host(self.keys), res.keys, KEY_RTOL, name + ": keys")
+        assert_same_bits(host(self.gd), res.gbar, name + ": gbar")
+        assert_same_bits(host(self.wd), w_ref, name + ": w")
+        assert_same_bits(host(self.vd), v_ref, name + ": v")
+        assert_residual(self.flush(scratch), r_ref, self.plan.P, name + ": flushed residual")
+
+
+@pytest.mark.parametrize("depth,steps,resume_after", [(1, 5, 3), (2, 4, None)])
+def test_sparse_alexnet128_full_size_deferred(ga, depth, steps, resume_after):
+    """The benchmarked deferred form at full size, every output against the
+    oracle at every step (the residual through a flush into a copy).  With
+    resume_after, a second run beside it is checkpointed after that step:
+    flushed in place, its residual, weights and velocity copied to the host,
+    the device buffers dropped, and resumed from the host copies alone (age 0,
+    no mask, no earlier gradient tensor); it must match the oracle (and so the
+    straight run) at every later step.  At depth 2 one more step is repeated
+    five times from the same saved state and must give bitwise identical
+    keys, masks, mean gradient, weights, velocity and flushed residual."""
     wl = workloads.WORKLOADS["alexnet128_sparse"]
     C = wl.chunk
     plan = ga.Plan(wl.W, wl.numels, True, chunk=C, keep_ratio=wl.rho)
-    P, ld, k, n_c = wl.P, plan.ld, plan.k, plan.n_chunks
+    P, ld, k = wl.P, plan.ld, plan.k
     seg = workloads.segments(wl)
     w_ref = workloads.weights(wl)
     v_ref = np.zeros(P, np.float32)
     r_ref = np.zeros((wl.W, ld), np.float32)
-    wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
-    rd = plan.empty_residual()
-    keys = plan.empty_keys()
-    idx = torch.empty((wl.W, k), dtype=torch.int32, device="cuda")
-    masks = [torch.zeros((wl.W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(3)]
-    gd = torch.empty(P, dtype=torch.float32, device="cuda")
-    sample = [0, 1, 63, 127]
-    prev_layers = []
+    runs = {"straight": DeviceRun(plan, w_ref)}
+    if resume_after:
+        runs["resumed"] = DeviceRun(plan, w_ref)
+    scratch = plan.empty_residual()
+    kept = []
     for step in range(1, steps + 1):
         t0 = time.time()
         b = workloads.grad_bucket(wl, step, ld, seg=seg)
         buf, ptrs = device_layers(b[:, :P], wl.numels)
+        kept = (kept + [buf])[-(depth + 1):]
         res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         del b
-        prev, cur = masks[(step + 1) % 2], masks[step % 2]
-        if mode == "pending2":
-            cur, prev, prev2 = masks[step % 3], masks[(step + 2) % 3], masks[(step + 1) % 3]
-        r_view = rd
-        if mode == "defer":
-            plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
-            plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
-        elif mode == "pending2":
-            pptrs = prev_layers[-1][1] if prev_layers else ptrs
-            ppptrs = prev_layers[-2][1] if len(prev_layers) > 1 else ptrs
-            plan.chunk_norm_layers_pending2(ptrs, pptrs, ppptrs, rd, keys, prev, prev2, cur)
-            plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce_layers_pending2(ptrs, pptrs, rd, prev, cur, prev2, gd, wd, vd, wl.lr, wl.mu)
-            r_view = rd.clone()
-            plan.residual_flush_layers2(ptrs, pptrs, r_view, prev, cur, prev2)
-            prev_layers = (prev_layers + [(buf, ptrs)])[-2:]
-        else:
-            pptrs = prev_layers[-1][1] if prev_layers else ptrs
-            plan.chunk_norm_layers_pending(ptrs, pptrs, rd, keys, prev, cur)
-            plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
-            r_view = rd.clone()
-            plan.residual_flush_layers(ptrs, r_view, prev, cur)
-            prev_layers = [(buf, ptrs)]
-        torch.cuda.synchronize()
-        del buf
         assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
-        assert np.array_equal(host(idx), res.sel_idx), "selected chunk indices differ"
-        assert np.array_equal(host(cur).view(np.uint32), res.sel_mask)
-        assert_close(host(keys), res.keys, KEY_RTOL, "keys")
-        assert_same_bits(host(gd), res.gbar, "gbar")
-        assert_same_bits(host(wd), w_ref, "w")
-        assert_same_bits(host(vd), v_ref, "v")
-        m = host(cur).view(np.uint32)
-        for w in sample:
-            r = host(r_view[w, :P]).copy()
-            for c in range(n_c):
-                if (int(m[w, c >> 5]) >> (c & 31)) & 1:
-                    r[c * C:min((c + 1) * C, P)] = 0.0
-            assert_same_bits(r, r_ref[w, :P], "residual of worker %d" % w)
-        del r_view
-        log("%s step %d compared in %.1fs" % (mode, step, time.time() - t0))
+        for name, run in runs.items():
+            run.step(ptrs, depth, wl.lr, wl.mu)
+            torch.cuda.synchronize()
+            run.check(res, w_ref, v_ref, r_ref, scratch, "depth %d %s step %d" % (depth, name, step))
+        if resume_after and step == resume_after:
+            old = runs["resumed"]
+            old.flush(old.rd)
+            torch.cuda.synchronize()
+            saved = (host(old.rd).copy(), host(old.wd).copy(), host(old.vd).copy())
+            del runs["resumed"], old
+            torch.cuda.empty_cache()
+            new = DeviceRun(plan, saved[1])
+            new.rd.copy_(torch.from_numpy(saved[0]))
+            new.vd.copy_(torch.from_numpy(saved[2]))
+            del saved
+            runs["resumed"] = new          # age 0, no mask, no earlier tensor
+            log("depth %d: checkpoint after step %d, resumed from the host copy" % (depth, step))
+        log("depth %d step %d compared in %.1fs" % (depth, step, time.time() - t0))
+    if depth == 2:
+        # determinism: the next step five times from one saved state
+        run = runs["straight"]
+        b = workloads.grad_bucket(wl, steps + 1, ld, seg=seg)
+        buf, ptrs = device_layers(b[:, :P], wl.numels)
+        del b
+        kept = (kept + [buf])[-(depth + 1):]
+        state = (run.rd.clone(), run.wd.clone(), run.vd.clone(), list(run.masks), list(run.tables))
+        outs = []
+        for rep in range(5):
+            run.rd.copy_(state[0])
+            run.wd.copy_(state[1])
+            run.vd.copy_(state[2])
+            run.masks, run.tables = list(state[3]), list(state[4])
+            run.step(ptrs, depth, wl.lr, wl.mu)
+            got = [run.keys.clone(), run.masks[0].clone(), run.gd.clone(), run.wd.clone(), run.vd.clone()]
+            run.flush(scratch)
+            torch.cuda.synchronize()
+            if rep == 0:
+                outs = got
+                first_r = scratch.clone()
+            else:
+                for a, b_ in zip(outs, got):
+                    assert torch.equal(a.view(torch.int32) if a.dtype != torch.float64 else a.view(torch.int64),
+                                       b_.view(torch.int32) if b_.dtype != torch.float64 else b_.view(torch.int64))
+                assert torch.equal(scratch.view(torch.int32), first_r.view(torch.int32))
+        log("depth 2: step %d repeated 5 times, bitwise identical" % (steps + 1))

@@ -3,9 +3,9 @@ path that applies to it and compared with the oracle element by element:
 random worker counts, layer lists (aligned and ragged sizes, small and large
 layers), binary16 or binary32 gradients, chunk sizes and keep ratios, both
 residual modes, zero-copy tensors at random misalignments, and multi-bucket
-schedules at random thresholds, the deferred residual form where it applies
-(plain, or pending at depth 1 or 2, its residual checked through a flushed
-copy).
+schedules at random thresholds, and the deferred residual form where it
+applies (a random depth and store schedule, layer tensors whose alignment
+changes from step to step, the residual checked through a flushed copy).
 The case is printed before it runs."""
 import numpy as np
 import pytest
@@ -50,9 +50,9 @@ def draw(seed):
     deferred = bool(sparse and chunk % 256 == 0 and rng.random() < 0.7)
     mis = int(rng.integers(0, 4))
     thr = int(rng.choice([1, 64, 1024, 16384, 1 << 30]))
-    form = str(rng.choice(["defer", "pending", "pending2"])) if deferred else None
+    depth = int(rng.integers(0, 3)) if deferred else None
     return dict(W=W, numels=numels, fp16=fp16, sparse=sparse, chunk=chunk, rho=rho, lazy=lazy or deferred,
-                deferred=deferred, mis=mis, thr=thr, form=form)
+                deferred=deferred, mis=mis, thr=thr, depth=depth)
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
@@ -95,41 +95,37 @@ def test_random_case(ga, seed):
     wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
     rd, keys = plan.empty_residual(), plan.empty_keys()
     idx = torch.full((W, max(k, 1)), -1, dtype=torch.int32, device="cuda")
-    masks = [torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda") for _ in range(3)]
+    mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
     gd = torch.empty(P, dtype=torch.float32, device="cuda")
-    kept = []               # the previous steps' tensors (pending forms)
-    form = c["form"]
-    for step in range(1, 5 if form in ("pending", "pending2") else 4):
+    depth = c["depth"]
+    rng = np.random.default_rng(5000 + seed)
+    hist_masks, hist_tables, kept = [None], [], []
+    for step in range(1, 6 if depth is not None else 4):
         b = workloads.grad_bucket(wl, step, ld)
         res = oracle.sparse_step(b, P, fp16, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
-        cur, prev = masks[step % 2], masks[(step + 1) % 2]
-        if form == "pending2":
-            cur, prev, prev2 = masks[step % 3], masks[(step + 2) % 3], masks[(step + 1) % 3]
-        buf, ptrs = device_layers(b[:, :P], numels, misalign)
+        mis_t = (lambda w, l: 0) if c["mis"] == 0 else (lambda w, l: (c["mis"] * w + l + step) % 4)
+        buf, ptrs = device_layers(b[:, :P], numels, mis_t)
         r_view = rd
-        p1 = kept[-1][1] if kept else ptrs
-        p2 = kept[-2][1] if len(kept) > 1 else ptrs
-        if form == "pending":
-            plan.chunk_norm_layers_pending(ptrs, p1, rd, keys, prev, cur)
+        cur = mask
+        if depth is not None:
+            # a random store schedule that never holds more than `depth` earlier steps
+            age = len(hist_masks) - 1
+            store = age >= depth or bool(rng.random() < 0.3)
+            hist = plan.history(hist_masks, hist_tables)
+            cur = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
+            plan.chunk_norm_deferred(ptrs, hist, store, rd, keys)
             plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce_layers_pending(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+            plan.sparse_gather_reduce_deferred(ptrs, hist, store, rd, cur, gd, wd, vd, wl.lr, wl.mu)
             r_view = rd.clone()
-            plan.residual_flush_layers(ptrs, r_view, prev, cur)
-        elif form == "pending2":
-            plan.chunk_norm_layers_pending2(ptrs, p1, p2, rd, keys, prev, prev2, cur)
-            plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce_layers_pending2(ptrs, p1, rd, prev, cur, prev2, gd, wd, vd, wl.lr, wl.mu)
-            r_view = rd.clone()
-            plan.residual_flush_layers2(ptrs, p1, r_view, prev, cur, prev2)
-        elif form == "defer":
-            plan.chunk_norm_layers_defer(ptrs, rd, keys, prev)
-            plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce_layers_defer(ptrs, rd, prev, cur, gd, wd, vd, wl.lr, wl.mu)
+            plan.residual_flush(ptrs, hist, store, r_view, cur)
+            if store:
+                hist_masks, hist_tables, kept = [cur], [], []
+            else:
+                hist_masks, hist_tables, kept = [cur] + hist_masks, [ptrs] + hist_tables, [buf] + kept
         else:
-            plan.chunk_norm_layers(ptrs, rd, keys, prev if (c["lazy"] and step > 1) else None)
-            plan.chunk_topk(keys, idx, cur)
-            plan.sparse_gather_reduce(rd, cur, not c["lazy"], gd, wd, vd, wl.lr, wl.mu)
-        kept = (kept + [(buf, ptrs)])[-2:]
+            plan.chunk_norm_layers(ptrs, rd, keys, mask if (c["lazy"] and step > 1) else None)
+            plan.chunk_topk(keys, idx, mask)
+            plan.sparse_gather_reduce(rd, mask, not c["lazy"], gd, wd, vd, wl.lr, wl.mu)
         torch.cuda.synchronize()
         if not np.all(res.margin > 1e-12):
             pytest.skip("selection boundary too close to certify at seed %d" % seed)
