@@ -21,11 +21,12 @@
 //                  (binary64 sum of squares) and, on a storing step, writes a
 //                  into R; as the flush, writes the residual itself (zero on
 //                  the chunks sent this step).
-//   k_gather_hist  one wavefront per 256 elements of one chunk: the fixed
+//   k_gather_hist  one wavefront per 256 or 512 elements of one chunk: the fixed
 //                  binary tree over the workers' sent values (absent workers
-//                  are +0), the mean and the fused momentum-SGD update.  A sent
-//                  value is read from R on a storing step, else re-formed as
-//                  above.
+//                  are +0), the mean and the fused momentum-SGD update, on a
+//                  step that did not store: every sent value is re-formed as
+//                  above.  On a storing step the sent values are R itself, and
+//                  the lazy-zero gather (k_gather_wave) reduces them.
 //
 // With age 0 and a store every step this is the lazy-zero form of the
 // residual: the selection mask of the previous step stands for the zeroing.
@@ -244,16 +245,31 @@ hipError_t norm_launch(const Plan& p, const HistArgs& h, bool store, bool flush,
 // k_gather_hist
 // ---------------------------------------------------------------------------
 
-// Four elements of worker wk's gradient at i0 (i0 % 4 == 0) through a layer
-// table, element by element (zero past P): for tensors not aligned for a
-// vector load, and for wavefronts that straddle layers (la: the lane's layer,
-// ea: its end).
-template <bool FP16>
-__device__ __noinline__ float4 grad4_slow(const uint64_t* __restrict__ table, const int64_t* __restrict__ offsets,
-                                          int32_t L, int32_t wk, int32_t la, int64_t ea, int64_t i0, int64_t P) {
-    float f[4] = {0.f, 0.f, 0.f, 0.f};
+// A lane's E gradient elements of one worker as raw bits: binary16 two to a
+// word (NW = E/2 words), binary32 one to a word (NW = E).
+template <bool FP16, int E>
+struct GradBits {
+    static constexpr int NW = FP16 ? E / 2 : E;
+    uint32_t w[NW];
+
+    __device__ __forceinline__ float value(int e) const {
+        if (FP16) return widen1((uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+        return __uint_as_float(w[e]);
+    }
+};
+
+// Elements i0 .. i0+E-1 of worker wk's gradient through a layer table, element
+// by element (zero past P): for tensors not aligned for a vector load, and for
+// wavefronts that straddle layers (la: the lane's layer at i0, ea: its end).
+template <bool FP16, int E>
+__device__ __noinline__ GradBits<FP16, E> grad_slow(const uint64_t* __restrict__ table,
+                                                    const int64_t* __restrict__ offsets, int32_t L, int32_t wk,
+                                                    int32_t la, int64_t ea, int64_t i0, int64_t P) {
+    GradBits<FP16, E> x;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int q = 0; q < GradBits<FP16, E>::NW; ++q) x.w[q] = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
         const int64_t i = i0 + e;
         if (i < P) {
             int32_t l = la;
@@ -263,31 +279,39 @@ __device__ __noinline__ float4 grad4_slow(const uint64_t* __restrict__ table, co
             }
             const uint64_t a = table[(int64_t)wk * L + l];
             const int64_t j = i - offsets[l];
-            f[e] = FP16 ? widen1(as_global<uint16_t>(a)[j]) : as_global<float>(a)[j];
+            if (FP16) x.w[e >> 1] |= (uint32_t)as_global<uint16_t>(a)[j] << ((e & 1) * 16);
+            else x.w[e] = as_global<uint32_t>(a)[j];
         }
     }
-    return make_float4(f[0], f[1], f[2], f[3]);
+    return x;
 }
 
-// Worker wk's four gradient elements at the lane's offset: a vector load from
-// the address lane b of `mine` holds (vec), else element by element.
-template <bool FP16>
-__device__ __forceinline__ float4 grad4(bool vec, uint64_t mine, int b, int64_t byte_off,
-                                        const uint64_t* __restrict__ table, const int64_t* __restrict__ offsets,
-                                        int32_t L, int32_t wk, int32_t la, int64_t ea, int64_t i0, int64_t P) {
+// Worker wk's gradient at the lane's elements: one vector load (E*b bytes,
+// 8 or 16) from the address lane b of `mine` holds (vec), else element by
+// element.
+template <bool FP16, int E>
+__device__ __forceinline__ GradBits<FP16, E> grad_bits(bool vec, uint64_t mine, int b, int64_t byte_off,
+                                                       const uint64_t* __restrict__ table,
+                                                       const int64_t* __restrict__ offsets, int32_t L, int32_t wk,
+                                                       int32_t la, int64_t ea, int64_t i0, int64_t P) {
+    constexpr int NW = GradBits<FP16, E>::NW;
+    static_assert(NW == 2 || NW == 4, "8- or 16-byte loads");
     if (vec) {
         const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(mine >> 32), b) << 32) |
                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, b);
         const uint64_t addr = base + (uint64_t)byte_off;
-        if (FP16) {
+        GradBits<FP16, E> x;
+        if (NW == 4) {
+            const u32x4 t = *as_global<u32x4>(addr);
+            x.w[0] = t.x; x.w[1] = t.y; x.w[NW > 2 ? 2 : 0] = t.z; x.w[NW > 3 ? 3 : 0] = t.w;
+        } else {
             typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-            const v2u x = *as_global<v2u>(addr);
-            return make_float4(widen1((uint16_t)(x.x & 0xffffu)), widen1((uint16_t)(x.x >> 16)),
-                               widen1((uint16_t)(x.y & 0xffffu)), widen1((uint16_t)(x.y >> 16)));
+            const v2u t = *as_global<v2u>(addr);
+            x.w[0] = t.x; x.w[1] = t.y;
         }
-        return load_f4(as_global<void>(addr));
+        return x;
     }
-    return grad4_slow<FP16>(table, offsets, L, wk, la, ea, i0, P);
+    return grad_slow<FP16, E>(table, offsets, L, wk, la, ea, i0, P);
 }
 
 // The residual case of the worker at bit b of a group: sent j steps back
@@ -305,18 +329,113 @@ __device__ __forceinline__ void leaf_case(const uint64_t (&mh)[AGE + 1], int32_t
         }
 }
 
-// STORED: this step's norm pass wrote a into R, so every sent value is read
-// from R; otherwise each is re-formed from the gradients and R (age <= AGE).
-template <int LEV, bool FP16, bool STORED, int AGE>
+// What a wavefront needs of one 64-worker group: the bitmaps of the workers
+// that send the chunk now (mc) and that sent it j+1 steps back (mh[j]), and,
+// for a tile inside one layer, lane l's worker's tensor address of that layer
+// in each step's table (ad[j]) with whether every address of the group allows
+// a vector load (vec[j]).
+template <int AGE>
+struct Group {
+    uint64_t mc;
+    uint64_t mh[AGE + 1];
+    uint64_t ad[AGE + 1];
+    bool vec[AGE + 1];
+};
+
+// The raw words behind a Group, loaded first so that the loads of several
+// groups are in flight together.
+template <int AGE>
+struct GroupWords {
+    uint32_t hw[AGE + 1];
+    uint64_t ad[AGE + 1];
+};
+
+template <int AGE>
+__device__ __forceinline__ void group_issue(const HistArgs& h, int32_t W, int32_t mw, int32_t cw, int32_t L,
+                                            int32_t l0, bool whole, int32_t wk, GroupWords<AGE>& gw) {
+    const bool in = wk < W;
+#pragma unroll
+    for (int j = 0; j <= AGE; ++j) {
+        gw.hw[j] = (in && j <= h.age && h.masks[j] != nullptr) ? h.masks[j][(int64_t)wk * mw + cw] : 0u;
+        gw.ad[j] = (in && whole && j <= h.age) ? h.layers[j][(int64_t)wk * L + l0] : 0ull;
+    }
+}
+
+// vec[j] holds only for a whole tile (otherwise no address was loaded and
+// every lane finds its own layer) whose group's addresses are all aligned to
+// the load width.
+template <int AGE>
+__device__ __forceinline__ void group_finish(const GroupWords<AGE>& gw, uint32_t cb, uint64_t mc, bool whole,
+                                             uint64_t align_mask, Group<AGE>& g) {
+    g.mc = mc;
+#pragma unroll
+    for (int j = 0; j <= AGE; ++j) {
+        g.mh[j] = __ballot((gw.hw[j] & cb) != 0u);
+        g.ad[j] = gw.ad[j];
+        g.vec[j] = whole && __ballot((gw.ad[j] & align_mask) != 0ull) == 0ull;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T pick4(int gi, const T (&a)[4]) {
+    return gi == 0 ? a[0] : gi == 1 ? a[1] : gi == 2 ? a[2] : a[3];
+}
+
+// The (at most four) groups of W < 256 workers, field by field, so that every
+// array index is a constant and the state stays in registers.
+template <int AGE>
+struct Groups4 {
+    uint64_t mc[4];
+    uint64_t mh[AGE + 1][4];
+    uint64_t ad[AGE + 1][4];
+    bool vec[AGE + 1][4];
+
+    __device__ __forceinline__ void set(int gi, const Group<AGE>& g) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q == gi) {
+                mc[q] = g.mc;
+#pragma unroll
+                for (int j = 0; j <= AGE; ++j) {
+                    mh[j][q] = g.mh[j];
+                    ad[j][q] = g.ad[j];
+                    vec[j][q] = g.vec[j];
+                }
+            }
+    }
+
+    __device__ __forceinline__ void get(int gi, Group<AGE>& g) const {
+        g.mc = pick4(gi, mc);
+#pragma unroll
+        for (int j = 0; j <= AGE; ++j) {
+            g.mh[j] = pick4(gi, mh[j]);
+            g.ad[j] = pick4(gi, ad[j]);
+            g.vec[j] = pick4(gi, vec[j]);
+        }
+    }
+};
+
+// The gather-reduce of a step whose norm pass did not store: every sent value
+// is re-formed, a = g_t + (g_{t-1} + (... + base)), from this step's gradient
+// tensors, the n earlier ones its case needs and, unless its base is +0, R.
+// (A storing step's values are R itself: that is the lazy-zero gather.)
+// A wavefront covers 64*E elements of one chunk, E per lane (E = 8 for
+// binary16 gradients when the chunk size allows it: 16-byte gradient loads).
+// For W < 256 the (at most four) groups' bitmaps and addresses are loaded
+// once, together, and kept in registers; w and v are requested first.
+// Gradients stay raw bits until their leaf is formed.
+template <int LEV, bool FP16, int AGE, int E>
 __global__ __launch_bounds__(kGatherThreads) void k_gather_hist(
     HistArgs h, const int64_t* __restrict__ offsets, const uint32_t* __restrict__ tile_layer, int64_t tile_elems,
     int32_t L, const float* __restrict__ resid, int64_t ld, int32_t W, int64_t P, int64_t C,
     const uint32_t* __restrict__ sel, int32_t mw, float invW, float* __restrict__ grad, int32_t do_sgd, float lr,
     float mu, float* __restrict__ w, float* __restrict__ v) {
-    constexpr int E = 4;
-    constexpr int UNR = STORED ? 16 : 8;   // leaves in flight
+    static_assert(E == 4 || E == 8, "4 or 8 elements per lane");
+    constexpr int UNR = E == 8 ? 4 : 8;   // leaves in flight
+    constexpr int G = LEV <= 8 ? 4 : 1;   // groups kept in registers
     constexpr int64_t kEsz = FP16 ? 2 : 4;
-    constexpr uint64_t kAlignMask = FP16 ? 7ull : 15ull;
+    constexpr int E4 = E / 4;
+    constexpr uint64_t kAlignMask = (uint64_t)(E * kEsz >= 16 ? 15 : 7);
     const int lane = threadIdx.x & 63;
     const int64_t wave_base =
         ((int64_t)blockIdx.x * kGatherThreads + (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x & ~63u)) * E;
@@ -328,21 +447,38 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_hist(
     const int32_t cw = c >> 5;
     const uint32_t cb = 1u << (c & 31);
 
-    // did any worker send this chunk?
-    bool any = false;
-    for (int32_t g0 = 0; g0 < W; g0 += 64) {
-        const int32_t wk = g0 + lane;
-        const uint32_t sw = wk < W ? sel[(int64_t)wk * mw + cw] : 0u;
-        any |= __ballot((sw & cb) != 0u) != 0ull;
-    }
-
-    float4 wv = make_float4(0.f, 0.f, 0.f, 0.f), vv = wv;
+    float4 wv[E4], vv[E4];
+#pragma unroll
+    for (int q = 0; q < E4; ++q) wv[q] = vv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (do_sgd && full) {
-        wv = *reinterpret_cast<const float4*>(w + i0);
-        vv = *reinterpret_cast<const float4*>(v + i0);
+#pragma unroll
+        for (int q = 0; q < E4; ++q) {
+            wv[q] = *reinterpret_cast<const float4*>(w + i0 + 4 * q);
+            vv[q] = *reinterpret_cast<const float4*>(v + i0 + 4 * q);
+        }
+    }
+    // this step's mask words of the first G groups, in flight together
+    uint32_t sw[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        const int32_t wk = gi * 64 + lane;
+        sw[gi] = wk < W ? sel[(int64_t)wk * mw + cw] : 0u;
+    }
+    uint64_t mc[G];
+    bool any = false;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        mc[gi] = __ballot((sw[gi] & cb) != 0u);
+        any |= mc[gi] != 0ull;
+    }
+    for (int32_t g0 = G * 64; g0 < W; g0 += 64) {
+        const int32_t wk = g0 + lane;
+        any |= __ballot(wk < W && (sel[(int64_t)wk * mw + cw] & cb) != 0u) != 0ull;
     }
 
-    float s[E] = {0.f, 0.f, 0.f, 0.f};
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = 0.f;
     if (any) {
         // the layer of the wavefront's tile; a tile that lies in one layer at a
         // vector-aligned offset is whole, otherwise each lane finds its layer
@@ -352,7 +488,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_hist(
         const int64_t off0 = offsets[l0];
         int32_t la = l0;
         int64_t ea = offsets[l0 + 1];
-        if (!STORED && !whole && valid) {
+        if (!whole && valid) {
             int32_t lo = l0, hi = L;
             while (lo < hi) {
                 const int32_t mid = (lo + hi) >> 1;
@@ -364,88 +500,78 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_hist(
         }
         const int64_t byte_off = (i0 - off0) * kEsz;
 
+        Groups4<AGE> gs;
+        if (G == 4) {
+            GroupWords<AGE> gw[4];
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) group_issue<AGE>(h, W, mw, cw, L, l0, whole, gi * 64 + lane, gw[gi]);
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                Group<AGE> g;
+                group_finish<AGE>(gw[gi], cb, mc[gi < G ? gi : 0], whole, kAlignMask, g);
+                gs.set(gi, g);
+            }
+        }
+
         TreeAcc<LEV, E> tree;
         uint32_t cnt = 0;
         for (int32_t g0 = 0; g0 < W; g0 += 64) {
-            const int32_t wk = g0 + lane;
-            const bool in = wk < W;
-            const uint64_t mc = __ballot(in && (sel[(int64_t)wk * mw + cw] & cb) != 0u);
-            uint64_t mh[AGE + 1];
-            uint64_t ad[AGE + 1];
-            bool vec[AGE + 1];
-#pragma unroll
-            for (int j = 0; j <= AGE; ++j) {
-                mh[j] = 0ull;
-                ad[j] = 0ull;
-                vec[j] = false;
-            }
-            if (!STORED && mc != 0ull) {
-#pragma unroll
-                for (int j = 0; j <= AGE; ++j)
-                    if (j <= h.age && h.masks[j] != nullptr)
-                        mh[j] = __ballot(in && (h.masks[j][(int64_t)wk * mw + cw] & cb) != 0u);
-                // which gradient tables this group's sent leaves read: this
-                // step's always, one step back when n >= 1, two when n >= 2
-                if (whole) {
-#pragma unroll
-                    for (int j = 0; j <= AGE; ++j) {
-                        if (j > h.age) continue;
-                        ad[j] = in ? h.layers[j][(int64_t)wk * L + l0] : 0ull;
-                        vec[j] = __ballot((ad[j] & kAlignMask) != 0ull) == 0ull;
-                    }
-                }
+            Group<AGE> g;
+            if (G == 4) {
+                gs.get(g0 >> 6, g);
+            } else {
+                const int32_t wk = g0 + lane;
+                const uint32_t sw1 = wk < W ? sel[(int64_t)wk * mw + cw] : 0u;
+                GroupWords<AGE> gw;
+                group_issue<AGE>(h, W, mw, cw, L, l0, whole, wk, gw);
+                group_finish<AGE>(gw, cb, __ballot((sw1 & cb) != 0u), whole, kAlignMask, g);
             }
             const int32_t gn = W - g0 < 64 ? W - g0 : 64;
             for (int32_t u0 = 0; u0 < gn; u0 += UNR) {
-                float4 xr[UNR], x0[UNR], x1[UNR], x2[UNR];
+                float4 xr[UNR][E4];
+                GradBits<FP16, E> x0[UNR], x1[UNR], x2[UNR];
                 // every load of the batch first ...
 #pragma unroll
                 for (int u = 0; u < UNR; ++u) {
                     const int32_t b = u0 + u;
-                    if (b >= gn || !((mc >> b) & 1ull) || !valid) continue;
-                    const float* rp = resid + (int64_t)(g0 + b) * ld + i0;
-                    if (STORED) {
-                        xr[u] = load_f4_nt(rp);
-                    } else {
-                        int32_t n;
-                        bool zero;
-                        leaf_case<AGE>(mh, h.age, b, n, zero);
-                        x0[u] = grad4<FP16>(vec[0], ad[0], b, byte_off, h.layers[0], offsets, L, g0 + b, la, ea, i0,
-                                            P);
-                        if (!zero) xr[u] = load_f4_nt(rp);
-                        if (AGE >= 1 && n >= 1)
-                            x1[u] = grad4<FP16>(vec[AGE >= 1 ? 1 : 0], ad[AGE >= 1 ? 1 : 0], b, byte_off,
-                                                h.layers[AGE >= 1 ? 1 : 0], offsets, L, g0 + b, la, ea, i0, P);
-                        if (AGE >= 2 && n >= 2)
-                            x2[u] = grad4<FP16>(vec[AGE >= 2 ? 2 : 0], ad[AGE >= 2 ? 2 : 0], b, byte_off,
-                                                h.layers[AGE >= 2 ? 2 : 0], offsets, L, g0 + b, la, ea, i0, P);
+                    if (b >= gn || !((g.mc >> b) & 1ull) || !valid) continue;
+                    int32_t n;
+                    bool zero;
+                    leaf_case<AGE>(g.mh, h.age, b, n, zero);
+                    x0[u] = grad_bits<FP16, E>(g.vec[0], g.ad[0], b, byte_off, h.layers[0], offsets, L, g0 + b, la,
+                                               ea, i0, P);
+                    if (!zero) {
+                        const float* rp = resid + (int64_t)(g0 + b) * ld + i0;
+#pragma unroll
+                        for (int q = 0; q < E4; ++q) xr[u][q] = load_f4_nt(rp + 4 * q);
                     }
+                    if (AGE >= 1 && n >= 1)
+                        x1[u] = grad_bits<FP16, E>(g.vec[AGE >= 1 ? 1 : 0], g.ad[AGE >= 1 ? 1 : 0], b, byte_off,
+                                                   h.layers[AGE >= 1 ? 1 : 0], offsets, L, g0 + b, la, ea, i0, P);
+                    if (AGE >= 2 && n >= 2)
+                        x2[u] = grad_bits<FP16, E>(g.vec[AGE >= 2 ? 2 : 0], g.ad[AGE >= 2 ? 2 : 0], b, byte_off,
+                                                   h.layers[AGE >= 2 ? 2 : 0], offsets, L, g0 + b, la, ea, i0, P);
                 }
                 // ... then the values, in worker order, into the tree
 #pragma unroll
                 for (int u = 0; u < UNR; ++u) {
                     const int32_t b = u0 + u;
                     if (b >= gn) continue;
-                    float f[E] = {0.f, 0.f, 0.f, 0.f};
-                    if (((mc >> b) & 1ull) && valid) {
-                        if (STORED) {
-                            f[0] = xr[u].x; f[1] = xr[u].y; f[2] = xr[u].z; f[3] = xr[u].w;
-                        } else {
-                            int32_t n;
-                            bool zero;
-                            leaf_case<AGE>(mh, h.age, b, n, zero);
-                            const float4 bs = zero ? make_float4(0.f, 0.f, 0.f, 0.f) : xr[u];
-                            float4 acc = bs;
-                            if (AGE >= 2 && n >= 2) {
-                                acc.x = x2[u].x + acc.x; acc.y = x2[u].y + acc.y;
-                                acc.z = x2[u].z + acc.z; acc.w = x2[u].w + acc.w;
-                            }
-                            if (AGE >= 1 && n >= 1) {
-                                acc.x = x1[u].x + acc.x; acc.y = x1[u].y + acc.y;
-                                acc.z = x1[u].z + acc.z; acc.w = x1[u].w + acc.w;
-                            }
-                            f[0] = x0[u].x + acc.x; f[1] = x0[u].y + acc.y;
-                            f[2] = x0[u].z + acc.z; f[3] = x0[u].w + acc.w;
+                    float f[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) f[e] = 0.f;
+                    if (((g.mc >> b) & 1ull) && valid) {
+                        int32_t n;
+                        bool zero;
+                        leaf_case<AGE>(g.mh, h.age, b, n, zero);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const float4 r4 = xr[u][e >> 2];
+                            const float rb = (e & 3) == 0 ? r4.x : (e & 3) == 1 ? r4.y : (e & 3) == 2 ? r4.z : r4.w;
+                            float acc = zero ? 0.f : rb;
+                            if (AGE >= 2 && n >= 2) acc = x2[u].value(e) + acc;
+                            if (AGE >= 1 && n >= 1) acc = x1[u].value(e) + acc;
+                            f[e] = x0[u].value(e) + acc;
                         }
                     }
                     tree.push(f, cnt);
@@ -461,14 +587,19 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_hist(
 #pragma unroll
     for (int e = 0; e < E; ++e) g[e] = s[e] * invW;
     if (full) {
-        if (grad) *reinterpret_cast<float4*>(grad + i0) = make_float4(g[0], g[1], g[2], g[3]);
-        if (do_sgd) {
-            sgd_update(g[0], lr, mu, wv.x, vv.x);
-            sgd_update(g[1], lr, mu, wv.y, vv.y);
-            sgd_update(g[2], lr, mu, wv.z, vv.z);
-            sgd_update(g[3], lr, mu, wv.w, vv.w);
-            *reinterpret_cast<float4*>(w + i0) = wv;
-            *reinterpret_cast<float4*>(v + i0) = vv;
+#pragma unroll
+        for (int q = 0; q < E4; ++q) {
+            if (grad)
+                *reinterpret_cast<float4*>(grad + i0 + 4 * q) =
+                    make_float4(g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]);
+            if (do_sgd) {
+                sgd_update(g[4 * q], lr, mu, wv[q].x, vv[q].x);
+                sgd_update(g[4 * q + 1], lr, mu, wv[q].y, vv[q].y);
+                sgd_update(g[4 * q + 2], lr, mu, wv[q].z, vv[q].z);
+                sgd_update(g[4 * q + 3], lr, mu, wv[q].w, vv[q].w);
+                *reinterpret_cast<float4*>(w + i0 + 4 * q) = wv[q];
+                *reinterpret_cast<float4*>(v + i0 + 4 * q) = vv[q];
+            }
         }
     } else {
         for (int e = 0; e < E; ++e) {
@@ -485,26 +616,29 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_hist(
     }
 }
 
-template <int LEV>
-hipError_t gather_launch(const Plan& p, const HistArgs& h, bool stored, const float* resid, const uint32_t* sel,
-                         float* grad, const ga_sgd* sgd, float* w, float* v, hipStream_t s) {
-    const int64_t threads = (p.P + 3) / 4;
+template <int LEV, int E>
+hipError_t gather_launch(const Plan& p, const HistArgs& h, const float* resid, const uint32_t* sel, float* grad,
+                         const ga_sgd* sgd, float* w, float* v, hipStream_t s) {
+    const int64_t threads = (p.P + E - 1) / E;
     const unsigned blocks = (unsigned)((threads + kGatherThreads - 1) / kGatherThreads);
     const float invW = (float)(1.0 / (double)p.W);
     const float lr = sgd ? sgd->lr : 0.f, mu = sgd ? sgd->mu : 0.f;
-#define GA_GH(F, ST, A)                                                                                            \
-    hipLaunchKernelGGL((k_gather_hist<LEV, F, ST, A>), dim3(blocks), dim3(kGatherThreads), 0, s, h, p.d_offsets,     \
-                       p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, sel, p.mw, invW, grad,       \
+#define GA_GH(F, A)                                                                                             \
+    hipLaunchKernelGGL((k_gather_hist<LEV, F, A, E>), dim3(blocks), dim3(kGatherThreads), 0, s, h, p.d_offsets,  \
+                       p.d_tile_layer, p.tile_elems, p.L, resid, p.ld, p.W, p.P, p.C, sel, p.mw, invW, grad,    \
                        sgd ? 1 : 0, lr, mu, w, v)
-#define GA_GH_AGE(F)                            \
-    do {                                        \
-        if (stored) GA_GH(F, true, 0);          \
-        else if (h.age == 0) GA_GH(F, false, 0); \
-        else if (h.age == 1) GA_GH(F, false, 1); \
-        else GA_GH(F, false, 2);                \
+#define GA_GH_AGE(F)                       \
+    do {                                   \
+        if (h.age == 0) GA_GH(F, 0);       \
+        else if (h.age == 1) GA_GH(F, 1);  \
+        else GA_GH(F, 2);                  \
     } while (0)
-    if (p.dtype == GA_FP16) GA_GH_AGE(true);
-    else GA_GH_AGE(false);
+    if constexpr (E == 8) {   // 8 elements per lane: binary16 only
+        GA_GH_AGE(true);
+    } else {
+        if (p.dtype == GA_FP16) GA_GH_AGE(true);
+        else GA_GH_AGE(false);
+    }
 #undef GA_GH_AGE
 #undef GA_GH
     return hipGetLastError();
@@ -544,9 +678,14 @@ hipError_t launch_gather_hist(const Plan& p, const HistArgs& h, bool stored, con
                               const uint32_t* sel, float* grad, const ga_sgd* sgd, float* w, float* v,
                               hipStream_t s) {
     if (p.P == 0) return hipSuccess;
-    if (p.W < (1 << 5)) return gather_launch<5>(p, h, stored, resid, sel, grad, sgd, w, v, s);
-    if (p.W < (1 << 8)) return gather_launch<8>(p, h, stored, resid, sel, grad, sgd, w, v, s);
-    return gather_launch<11>(p, h, stored, resid, sel, grad, sgd, w, v, s);
+    // a storing step left every a in R: the lazy-zero gather, which does not write R
+    if (stored) return launch_sparse_gather(p, const_cast<float*>(resid), sel, 0, grad, sgd, w, v, s);
+    // 4 elements per lane: 8 (16-byte binary16 loads, 512 elements per
+    // wavefront) measured slower at W = 128, its larger tree halving the
+    // wavefronts per SIMD
+    if (p.W < (1 << 5)) return gather_launch<5, 4>(p, h, resid, sel, grad, sgd, w, v, s);
+    if (p.W < (1 << 8)) return gather_launch<8, 4>(p, h, resid, sel, grad, sgd, w, v, s);
+    return gather_launch<11, 4>(p, h, resid, sel, grad, sgd, w, v, s);
 }
 
 }  // namespace ga
