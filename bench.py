@@ -32,6 +32,7 @@ import json
 import os
 import sys
 import time
+import types
 
 import numpy as np
 
@@ -68,6 +69,9 @@ def parse():
                     help="dense workloads: summation order (parameter server, ring) for comparison")
     ap.add_argument("--wire", choices=["f32", "f16"], default="f32",
                     help="dense workloads: binary16 wire (every value sent between workers rounded)")
+    ap.add_argument("--no-extras", dest="extras", action="store_false", default=True,
+                    help="skip the extra measurements of the default run (the step protocol and the lazy-zero "
+                         "sequence of the sparse workload, and the dense workloads)")
     ap.add_argument("--cpu-baseline", dest="cpu_baseline", action="store_true", default=True)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -125,6 +129,206 @@ def copy_calibration():
                       "GBps": (2 * n + 2 * plan.ld) / ms / 1e6}), flush=True)
 
 
+def load_batches(wl, plan, nb, layers_src, thr, keep_host_first):
+    """nb gradient batches generated on the host and made resident in HBM:
+    per-layer tensors (a layer table per batch) or packed [W][ld] buckets.
+    Returns (sources, kept layer tensors, first batch on the host or None)."""
+    import torch
+    import workloads
+    P, ld, W = wl.P, plan.ld, wl.W
+    seg = workloads.segments(wl)
+    gdt = torch.float16 if wl.fp16 else torch.float32
+    offs = np.cumsum([0] + wl.numels)
+    sources, keep = [], []
+    row = np.empty(P, np.uint16 if wl.fp16 else np.float32)
+    pinned = torch.empty(P, dtype=gdt).pin_memory()
+    host_first = np.zeros((W, ld), row.dtype) if keep_host_first else None
+    t0 = time.time()
+    for bi in range(nb):
+        if layers_src:
+            tensors = [[torch.empty(n, dtype=gdt, device="cuda") for n in wl.numels] for _ in range(W)]
+        else:
+            bucket = torch.zeros((W, ld), dtype=gdt, device="cuda")
+        for w in range(W):
+            workloads.grad_row(wl, bi + 1, w, seg, out=row, threads=thr)
+            pinned.numpy().view(row.dtype)[:] = row
+            if layers_src:
+                for l in range(len(wl.numels)):
+                    tensors[w][l].copy_(pinned[offs[l]:offs[l + 1]], non_blocking=False)
+            else:
+                bucket[w, :P].copy_(pinned, non_blocking=False)
+            if bi == 0 and host_first is not None:
+                host_first[w, :P] = row
+        if layers_src:
+            keep.append(tensors)
+            sources.append(torch.tensor([t.data_ptr() for tw in tensors for t in tw], dtype=torch.int64,
+                                        device="cuda"))
+        else:
+            sources.append(bucket)
+        log("%s: gradient batch %d resident (%.1fs)" % (wl.name, bi + 1, time.time() - t0))
+    return sources, keep, host_first
+
+
+def time_steps(step, n_warm, n_timed, n_kernels):
+    """Run n_warm + n_timed steps (step(t, events) records one event after each
+    of its n_kernels launches).  Returns (host ms per timed step, GPU-event ms
+    per timed step, [per timed step: [ms of each kernel]], [per timed step:
+    what step() returned])."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n = n_warm + n_timed
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)] for _ in range(n)]
+    ret = [None] * n
+
+    def one(t):
+        ev[t][0].record(stream)
+        ret[t] = step(t, ev[t][1:])
+
+    for t in range(n_warm):
+        one(t)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for t in range(n_warm, n):
+        one(t)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [[ev[t][j].elapsed_time(ev[t][j + 1]) for j in range(n_kernels)] for t in range(n)]
+    return wall * 1e3 / n_timed, t_start.elapsed_time(t_end) / n_timed, per, ret
+
+
+def sparse_stepper(plan, wl, sources, state, mode, depth, layers_src):
+    """A step function for time_steps over the sparse workload, and the object
+    holding its residual.  mode "deferred": the history form at `depth`;
+    "lazy": the lazy-zero sequence of the boundary's calls."""
+    import torch
+    import gradient_aggregation_amd as ga
+    nb = len(sources)
+    wd, vd = state
+    if mode == "deferred":
+        dr = ga.DeferredResidual(plan, depth)
+
+        def step(t, ev):
+            return dr.step(sources[t % nb], None, wd, vd, wl.lr, wl.mu, events=ev)
+        return step, dr
+    W = plan.W
+    holder = types.SimpleNamespace(
+        resid=plan.empty_residual(), keys=plan.empty_keys(),
+        idx=torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda"),
+        mask=torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda"), t0=None)
+
+    def step(t, ev):
+        b = sources[t % nb]
+        first = holder.t0 is None
+        if first:
+            holder.t0 = t
+        prev = None if first else holder.mask
+        if layers_src:
+            plan.chunk_norm_layers(b, holder.resid, holder.keys, prev)
+        else:
+            plan.chunk_norm(b, holder.resid, holder.keys, prev)
+        ev[0].record()
+        plan.chunk_topk(holder.keys, holder.idx, holder.mask)
+        ev[1].record()
+        plan.sparse_gather_reduce(holder.resid, holder.mask, False, None, wd, vd, wl.lr, wl.mu)
+        ev[2].record()
+        return True
+    return step, holder
+
+
+def kernel_stats(per, timed, names, stored=None):
+    out = {}
+    for j, nm in enumerate(names):
+        d = [per[t][j] for t in timed]
+        out[nm] = {"mean_ms": float(np.mean(d)), "min_ms": float(np.min(d)), "max_ms": float(np.max(d))}
+        if stored is not None and not all(stored[t] for t in timed):
+            for kind, want in (("storing", True), ("other", False)):
+                dk = [per[t][j] for t in timed if bool(stored[t]) == want]
+                if dk:
+                    out[nm]["mean_ms_%s_steps" % kind] = round(float(np.mean(dk)), 4)
+    return out
+
+
+def sparse_protocol(plan, wl, sources, w_init, mode, depth, layers_src, reps=5, steps=3):
+    """The step timing of the sparse workload's own protocol: `steps` steps from
+    a zero residual and fresh state, repeated `reps` times with the state reset
+    outside the timed region; per step, the median over the repetitions of the
+    whole step and of its two halves (norms + top-k | gather + SGD)."""
+    import torch
+    P, W = wl.P, wl.W
+    b_alg = W * P * ((2 if wl.fp16 else 4) + 8) + 16 * P
+    times = [[] for _ in range(steps)]
+    halves = [[] for _ in range(steps)]
+    for rep in range(reps):
+        wd = torch.from_numpy(w_init).cuda()
+        vd = torch.zeros(P, dtype=torch.float32, device="cuda")
+        step, holder = sparse_stepper(plan, wl, sources, (wd, vd), mode, depth, layers_src)
+        holder.resid.zero_()
+        torch.cuda.synchronize()
+        _, _, per, _ = time_steps(step, 0, steps, 3)
+        for t in range(steps):
+            times[t].append(sum(per[t]))
+            halves[t].append((per[t][0] + per[t][1], per[t][2]))
+        del step, holder, wd, vd
+        torch.cuda.empty_cache()
+    med = [float(np.median(x)) for x in times]
+    return {
+        "steps": steps, "repetitions": reps, "reset": "zero residual, fresh w and v, outside the timed region",
+        "step_ms_median": [round(x, 4) for x in med],
+        "norm_topk_ms_median": [round(float(np.median([h[0] for h in halves[t]])), 4) for t in range(steps)],
+        "gather_sgd_ms_median": [round(float(np.median([h[1] for h in halves[t]])), 4) for t in range(steps)],
+        "median_step_ms": round(float(np.median(med)), 4),
+        "alg_GBps_at_median_step": round(b_alg / (float(np.median(med)) * 1e-3) / 1e9, 1),
+        "pct_hbm_peak_alg_at_median_step": round(100.0 * b_alg / (float(np.median(med)) * 1e-3) / 1e9 /
+                                                 HBM_PEAK_GBPS, 2),
+        "mean_of_steps_ms": round(float(np.mean(med)), 4),
+        "note": "step 1 reads only the gradient (the residual is zero: described by an all-ones mask in the "
+                "deferred form, read from the zeroed buffer in the lazy form)",
+    }
+
+
+def dense_summary(thr, steps=200):
+    """The dense workloads (NiN W=32 binary32, GoogLeNet W=128 and AlexNet W=16
+    binary16), each from per-layer tensors read with zero copy: ms per step of
+    the fused tree + mean + SGD, algorithmic GB/s and % of peak, the fusion
+    copy (ga_bucket_pack) rate and the end-to-end time with that copy."""
+    import torch
+    import gradient_aggregation_amd as ga
+    import workloads
+    out = {}
+    for name in ("nin", "googlenet", "alexnet16"):
+        wl = workloads.WORKLOADS[name]
+        plan = ga.Plan(wl.W, wl.numels, wl.fp16)
+        sources, keep, _ = load_batches(wl, plan, 2, True, thr, False)
+        w_init = workloads.weights(wl, threads=thr)
+        states = [(torch.from_numpy(w_init).cuda(), torch.zeros(wl.P, dtype=torch.float32, device="cuda"))
+                  for _ in range(2)]
+
+        def step(t, ev):
+            wd, vd = states[t % 2]
+            plan.tree_reduce_layers(sources[t % 2], None, wd, vd, wl.lr, wl.mu)
+            ev[0].record()
+
+        ms, gms, per, _ = time_steps(step, 20, steps, 1)
+        b_in = 2 if wl.fp16 else 4
+        b_alg = wl.W * wl.P * b_in + 16 * wl.P
+        pack = time_pack(plan, wl, sources[-1], keep[-1], torch.cuda.current_stream())
+        kms = float(np.mean([per[t][0] for t in range(20, 20 + steps)]))
+        out[name] = {"W": wl.W, "P": wl.P, "grad_dtype": "f16" if wl.fp16 else "f32", "steps": steps,
+                     "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                     "alg_GBps": round(b_alg / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak_alg": round(100.0 * b_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                     "bytes_alg_per_step": b_alg, "pack_GBps": pack["GBps"], "pack_ms": pack["mean_ms"],
+                     "end_to_end_ms_with_pack": round(ms + pack["mean_ms"], 4)}
+        log("dense %s: %.4f ms/step (%.1f%% of peak)" % (name, ms, out[name]["pct_hbm_peak_alg"]))
+        del sources, keep, states
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +367,17 @@ def main():
     thr = host_threads()
     log("workload %s: W=%d P=%d ld=%d fp16=%s chunk=%d k=%d n_c=%d" % (
         wl.name, W, P, ld, wl.fp16, plan.chunk, plan.k, plan.n_chunks))
+    layers_src = args.source == "layers"
+    nb = max(1, args.batches)
+    deferred = False
+    if sparse:
+        deferred = args.residual == "deferred" and layers_src and plan.chunk % 256 == 0
+        if args.residual == "deferred" and not deferred:
+            log("the deferred form needs per-layer tensors and a chunk size that is a multiple of 256; "
+                "timing the lazy-zero sequence")
+        if deferred and nb < args.depth + 1:
+            print("--depth %d needs at least %d gradient batches" % (args.depth, args.depth + 1), file=sys.stderr)
+            sys.exit(2)
 
     # ---- inputs: generated on the host, made resident in HBM before timing ----
     # Default: every worker's gradient arrives as its own per-layer tensors (as
@@ -170,39 +385,7 @@ def main():
     # reading through the layer table.  --source bucket feeds a pre-packed
     # [W][ld] bucket instead.
     t0 = time.time()
-    seg = workloads.segments(wl)
-    nb = max(1, args.batches)
-    gdt = torch.float16 if wl.fp16 else torch.float32
-    offs = np.cumsum([0] + wl.numels)
-    layers_src = args.source == "layers"
-    sources = []            # per batch: int64 layer table (layers) or [W][ld] bucket
-    keep = []               # the layer tensors, kept alive
-    row = np.empty(P, np.uint16 if wl.fp16 else np.float32)
-    pinned = torch.empty(P, dtype=gdt).pin_memory()
-    # the CPU leg runs the oracle on the first batch, kept on the host
-    host_first = np.zeros((W, ld), row.dtype) if args.cpu_baseline else None
-    for bi in range(nb):
-        if layers_src:
-            tensors = [[torch.empty(n, dtype=gdt, device="cuda") for n in wl.numels] for _ in range(W)]
-        else:
-            bucket = torch.zeros((W, ld), dtype=gdt, device="cuda")
-        for w in range(W):
-            workloads.grad_row(wl, bi + 1, w, seg, out=row, threads=thr)
-            pinned.numpy().view(row.dtype)[:] = row
-            if layers_src:
-                for l in range(len(wl.numels)):
-                    tensors[w][l].copy_(pinned[offs[l]:offs[l + 1]], non_blocking=False)
-            else:
-                bucket[w, :P].copy_(pinned, non_blocking=False)
-            if bi == 0 and host_first is not None:
-                host_first[w, :P] = row
-        if layers_src:
-            keep.append(tensors)
-            sources.append(torch.tensor([t.data_ptr() for tw in tensors for t in tw], dtype=torch.int64,
-                                        device="cuda"))
-        else:
-            sources.append(bucket)
-        log("gradient batch %d resident (%.1fs)" % (bi + 1, time.time() - t0))
+    sources, keep, host_first = load_batches(wl, plan, nb, layers_src, thr, args.cpu_baseline)
     w_init = workloads.weights(wl, threads=thr)
     # Dense workloads: the w/v state (at most 0.5 GB) alternates between two
     # replicas, so the 256 MB Infinity Cache cannot serve a step's w and v
@@ -216,87 +399,30 @@ def main():
     gen_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
-    deferred = False
     if sparse:
-        deferred = args.residual == "deferred" and layers_src and plan.chunk % 256 == 0
-        if args.residual == "deferred" and not deferred:
-            log("the deferred form needs per-layer tensors and a chunk size that is a multiple of 256; "
-                "timing the lazy-zero sequence")
-        if deferred and nb < args.depth + 1:
-            print("--depth %d needs at least %d gradient batches" % (args.depth, args.depth + 1), file=sys.stderr)
-            sys.exit(2)
         names = ["chunk_norm", "topk", "gather_sgd"]
+        step, holder = sparse_stepper(plan, wl, sources, states[0], "deferred" if deferred else "lazy",
+                                      args.depth, layers_src)
     else:
         names = ["tree_sgd"]
-    n_steps = args.warmup + args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_steps)]
-    stored = [False] * n_steps
 
-    if sparse and deferred:
-        dr = ga.DeferredResidual(plan, args.depth)
-    elif sparse:
-        rd = plan.empty_residual()
-        keys = plan.empty_keys()
-        idx = torch.empty((W, max(plan.k, 1)), dtype=torch.int32, device="cuda")
-        mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
-
-    def step(t: int):
-        b = sources[t % nb]
-        wd, vd = states[t % n_state]
-        e = ev[t]
-        e[0].record(stream)
-        if sparse and deferred:
-            stored[t] = dr.step(b, None, wd, vd, wl.lr, wl.mu, events=e[1:])
-        elif sparse:
-            # the lazy-zero sequence of the boundary's calls: norms (zero-copy or
-            # from a bucket), top-k, gather-reduce without zeroing
-            if layers_src:
-                plan.chunk_norm_layers(b, rd, keys, mask if t > 0 else None)
-            else:
-                plan.chunk_norm(b, rd, keys, mask if t > 0 else None)
-            e[1].record(stream)
-            plan.chunk_topk(keys, idx, mask)
-            e[2].record(stream)
-            plan.sparse_gather_reduce(rd, mask, False, None, wd, vd, wl.lr, wl.mu)
-            e[3].record(stream)
-            stored[t] = True
-        else:
+        def step(t, ev):
+            b = sources[t % nb]
+            wd, vd = states[t % n_state]
             if variant:
                 plan.reduce_variant(b, args.order, args.wire == "f16", None, wd, vd, wl.lr, wl.mu)
             elif layers_src:
                 plan.tree_reduce_layers(b, None, wd, vd, wl.lr, wl.mu)
             else:
                 plan.tree_reduce(b, None, wd, vd, wl.lr, wl.mu)
-            e[1].record(stream)
+            ev[0].record()
+            return True
 
-    for t in range(args.warmup):
-        step(t)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for t in range(args.warmup, n_steps):
-        step(t)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    # ms_per_step is the host clock between the two synchronizations (launch
-    # overheads included); gpu_ms_per_step is the HIP-event span on the stream
-    gpu_ms_step = t_start.elapsed_time(t_end) / args.steps
-    ms_step = wall * 1e3 / args.steps
-    first_step = {nm: round(ev[0][j].elapsed_time(ev[0][j + 1]), 4) for j, nm in enumerate(names)}
-    per_kernel = {}
+    ms_step, gpu_ms_step, per, stored = time_steps(step, args.warmup, args.steps, len(names))
+    n_steps = args.warmup + args.steps
     timed = range(args.warmup, n_steps)
-    for j, nm in enumerate(names):
-        d = [ev[t][j].elapsed_time(ev[t][j + 1]) for t in timed]
-        per_kernel[nm] = {"mean_ms": float(np.mean(d)), "min_ms": float(np.min(d)), "max_ms": float(np.max(d))}
-        if sparse and deferred and args.depth > 0:
-            for kind, want in (("storing", True), ("other", False)):
-                dk = [ev[t][j].elapsed_time(ev[t][j + 1]) for t in timed if stored[t] == want]
-                if dk:
-                    per_kernel[nm]["mean_ms_%s_steps" % kind] = round(float(np.mean(dk)), 4)
+    first_step = {nm: round(per[0][j], 4) for j, nm in enumerate(names)}
+    per_kernel = kernel_stats(per, timed, names, stored if sparse else None)
     log("timed %d steps: %.3f ms/step (GPU events %.3f ms/step); %s" % (
         args.steps, ms_step, gpu_ms_step,
         ", ".join("%s %.3f ms" % (k, v["mean_ms"]) for k, v in per_kernel.items())))
@@ -304,10 +430,10 @@ def main():
     b_in = 2 if wl.fp16 else 4
     sel_stats = None
     if sparse and deferred:
-        sel_stats = selection_stats(plan, dr.masks[(dr.next - 2) % len(dr.masks)],
-                                    dr.masks[(dr.next - 1) % len(dr.masks)], P)
+        sel_stats = selection_stats(plan, holder.masks[(holder.next - 2) % len(holder.masks)],
+                                    holder.masks[(holder.next - 1) % len(holder.masks)], P)
     elif sparse:
-        sel_stats = selection_stats(plan, None, mask, P)
+        sel_stats = selection_stats(plan, None, holder.mask, P)
 
     pack = time_pack(plan, wl, sources[-1], keep[-1] if layers_src else None, stream)
 
@@ -338,10 +464,14 @@ def main():
     else:
         dom_kernel = "k_tree_layers" if layers_src else "k_tree"
     traffic_key = dom_kernel if not variant else "%s_order_%s_wire_%s" % (dom_kernel, args.order, args.wire)
-    if sparse and deferred:
-        traffic_key = "%s_depth%d" % (dom_kernel, args.depth)
-    traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name),
-                               traffic_key)
+    step_key = None
+    if sparse:
+        traffic_key = "%s_%s" % (dom_kernel, ("depth%d" % args.depth) if deferred else "lazy")
+        step_key = "step_%s" % (("depth%d" % args.depth) if deferred else "lazy")
+    tpath = args.traffic or os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
+    traffic = measured_traffic(tpath, traffic_key)
+    step_traffic = measured_traffic(tpath, step_key) if step_key else None
+    moved = None if traffic is None else traffic["bytes_per_launch"] / (dom_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -385,19 +515,54 @@ def main():
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             # the bytes the kernel moves (counters) over its time, beside the
             # algorithmic figure above
-            "moved_GBps": None if traffic is None else round(traffic["bytes_per_launch"] / (dom_ms * 1e-3) / 1e9, 1),
-            "moved_frac": None if traffic is None else round(
-                traffic["bytes_per_launch"] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "moved_GBps": None if moved is None else round(moved, 1),
+            "moved_frac": None if moved is None else round(moved / HBM_PEAK_GBPS, 4),
             "traffic_source": None if traffic is None else traffic["summary"],
             "bytes_per_launch": dom_bytes, "mean_launch_ms": round(dom_ms, 4),
             # the same chip's plain-copy rate in this run (the fusion copy of the
             # per-layer tensors, below): the measured ceiling for mixed read/write
             "vs_plain_copy": round(achieved / pack["GBps"], 3) if pack.get("GBps") else None,
         },
+        # the whole step by the counters: HBM bytes all its kernels move per
+        # step (averaged over the step kinds) over the step time
+        "step_moved": None if step_traffic is None else {
+            "bytes_per_step": step_traffic["bytes_per_launch"],
+            "GBps": round(step_traffic["bytes_per_launch"] / (ms_step * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * step_traffic["bytes_per_launch"] / (ms_step * 1e-3) / 1e9 /
+                                  HBM_PEAK_GBPS, 2),
+            "source": step_traffic["summary"]},
         "pack": pack,
         "ms_per_step_with_pack": round(ms_step + pack["mean_ms"], 4),
         "input_generation_s": round(gen_s, 1),
     }
+    if sparse:
+        del step, holder
+        torch.cuda.empty_cache()
+    if sparse and args.extras:
+        # the same workload under the survey's step protocol, and the lazy-zero
+        # sequence of the boundary's calls, on the same resident batches
+        result["protocol"] = {"deferred_depth%d" % args.depth if deferred else "lazy":
+                              sparse_protocol(plan, wl, sources, w_init, "deferred" if deferred else "lazy",
+                                              args.depth, layers_src)}
+        if deferred:
+            result["protocol"]["lazy"] = sparse_protocol(plan, wl, sources, w_init, "lazy", 0, layers_src)
+            lstep, lholder = sparse_stepper(plan, wl, sources, (torch.from_numpy(w_init).cuda(),
+                                                                torch.zeros(P, dtype=torch.float32, device="cuda")),
+                                            "lazy", 0, layers_src)
+            lms, lgms, lper, _ = time_steps(lstep, args.warmup, args.steps, 3)
+            result["lazy_sequence"] = {
+                "calls": "chunk_norm_layers -> chunk_topk -> sparse_gather_reduce (zero_selected=0)",
+                "ms_per_step": round(lms, 4), "alg_GBps": round(b_alg / (lms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak_alg": round(100.0 * b_alg / (lms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                "kernels": {k: round(v["mean_ms"], 4) for k, v in
+                            kernel_stats(lper, range(args.warmup, args.warmup + args.steps), names).items()}}
+            log("lazy-zero sequence: %.3f ms/step" % lms)
+            del lstep, lholder
+        log("protocol: %s" % {k: v["step_ms_median"] for k, v in result["protocol"].items()})
+    if args.extras:
+        del sources, keep, states
+        torch.cuda.empty_cache()
+        result["dense_workloads"] = dense_summary(thr)
 
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, plan, host_first, w_init, thr)
