@@ -2,15 +2,21 @@
  * A plain C client of libgradagg.so: no Python, no torch.  It drives the
  * dense step (fixed-tree reduce with fused momentum SGD) or the sparse step
  * (chunk norms + top-k, then gather-reduce with fused SGD) through the C ABI
- * of include/gradagg.h on device buffers it allocates itself, so that a test
- * can compare the results with the oracle.
+ * of include/gradagg.h on device buffers it allocates itself, then the two
+ * other calls of the path: the fusion of step 1's gradients, split into one
+ * device tensor per (worker, layer) at odd offsets, into a bucket
+ * (ga_bucket_pack), and one standalone momentum-SGD update of the final
+ * weights and velocity with the final mean gradient (ga_sgd_momentum_apply),
+ * so that a test can compare every result with the oracle.
  *
  * usage: abi_client <dir>
  *   <dir>/meta.txt   "W L fp16 chunk keep_ratio lr mu steps" then L layer sizes
  *   <dir>/bucket<s>.bin  step s's [W][ld] gradients (binary32, or binary16 bits)
  *   <dir>/w.bin      [P] binary32 initial weights (velocity starts at zero)
- * writes <dir>/gbar.bin, w_out.bin, v_out.bin (after the last step) and, for a
- * sparse plan, keys.bin, idx.bin, mask.bin, resid.bin of the last step.
+ * writes <dir>/gbar.bin, w_out.bin, v_out.bin (after the last step), pack.bin
+ * (the fused bucket of step 1), w_sgd.bin, v_sgd.bin (w_out, v_out after one
+ * more update with gbar) and, for a sparse plan, keys.bin, idx.bin,
+ * mask.bin, resid.bin of the last step.
  * Exit status 0 on success; a failed call prints ga_last_error() and exits 1.
  */
 #include <stdio.h>
@@ -140,6 +146,45 @@ int main(int argc, char** argv) {
     to_host(dir, "gbar.bin", d_grad, vec_bytes);
     to_host(dir, "w_out.bin", d_w, vec_bytes);
     to_host(dir, "v_out.bin", d_v, vec_bytes);
+
+    /* ga_sgd_momentum_apply: one more update of the final state with gbar */
+    GA(ga_sgd_momentum_apply(in.P, d_grad, d_w, d_v, &sgd, stream));
+    HIP(hipStreamSynchronize(stream));
+    to_host(dir, "w_sgd.bin", d_w, vec_bytes);
+    to_host(dir, "v_sgd.bin", d_v, vec_bytes);
+
+    /* ga_bucket_pack: step 1's gradients as W*L separate device tensors, each
+       starting (w + l) % 3 elements past its allocation, fused into a bucket */
+    {
+        unsigned char* h_b = (unsigned char*)read_file(dir, "bucket1.bin", bucket_bytes);
+        uint64_t* h_tab = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)W * (size_t)L);
+        void** allocs = (void**)malloc(sizeof(void*) * (size_t)W * (size_t)L);
+        for (int w = 0; w < W; ++w) {
+            size_t off = 0;
+            for (int l = 0; l < L; ++l) {
+                const size_t skew = (size_t)((w + l) % 3) * esz;
+                const size_t bytes = (size_t)numel[l] * esz;
+                unsigned char* d = (unsigned char*)dev_alloc(bytes + 3 * esz);
+                HIP(hipMemcpy(d + skew, h_b + ((size_t)w * (size_t)in.ld + off) * esz, bytes, hipMemcpyHostToDevice));
+                allocs[w * L + l] = d;
+                h_tab[w * L + l] = (uint64_t)(uintptr_t)(d + skew);
+                off += (size_t)numel[l];
+            }
+        }
+        uint64_t* d_tab = (uint64_t*)dev_alloc(sizeof(uint64_t) * (size_t)W * (size_t)L);
+        HIP(hipMemcpy(d_tab, h_tab, sizeof(uint64_t) * (size_t)W * (size_t)L, hipMemcpyHostToDevice));
+        void* d_packed = dev_alloc(bucket_bytes);
+        HIP(hipMemset(d_packed, 0xff, bucket_bytes));   /* the pack writes every byte, padding included */
+        GA(ga_bucket_pack(plan, d_tab, d_packed, stream));
+        HIP(hipStreamSynchronize(stream));
+        to_host(dir, "pack.bin", d_packed, bucket_bytes);
+        for (int q = 0; q < W * L; ++q) HIP(hipFree(allocs[q]));
+        HIP(hipFree(d_tab));
+        HIP(hipFree(d_packed));
+        free(allocs);
+        free(h_tab);
+        free(h_b);
+    }
     if (in.chunk > 0) {
         to_host(dir, "keys.bin", d_keys, (size_t)W * (size_t)in.n_chunks * 8);
         to_host(dir, "idx.bin", d_idx, (size_t)W * (size_t)in.k * 4);

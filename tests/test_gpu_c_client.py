@@ -1,6 +1,9 @@
 """The C ABI driven from plain C (tests/c/abi_client.c: gcc, libamdhip64, no
-Python or torch in the process): dense and sparse steps on device buffers the
-client allocates, compared with the oracle element by element."""
+Python or torch in the process): all five calls of the path - the fusion of
+per-layer tensors into a bucket, the dense tree reduce, the chunk norms with
+top-k, the sparse gather-reduce and the standalone momentum-SGD update - on
+device buffers the client allocates, compared with the oracle element by
+element."""
 import os
 import subprocess
 
@@ -54,6 +57,21 @@ def load(tmp_path, name, dtype):
     return np.fromfile(tmp_path / name, dtype=dtype)
 
 
+def check_pack_and_sgd(tmp_path, wl, ld, bucket1, gbar, w, v):
+    """pack.bin is the oracle's fusion of step 1's per-layer tensors (byte
+    for byte, zero padding); w_sgd/v_sgd are one more oracle update of the
+    final state with the final mean gradient."""
+    offs = np.cumsum([0] + list(wl.numels))
+    layers = [[bucket1[r, offs[l]:offs[l + 1]] for l in range(len(wl.numels))] for r in range(wl.W)]
+    ref = oracle.pack(layers, ld)
+    got = load(tmp_path, "pack.bin", ref.dtype).reshape(wl.W, ld)
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), "packed bucket differs"
+    w2, v2 = w.copy(), v.copy()
+    oracle.sgd(gbar, w2, v2, wl.lr, wl.mu)
+    assert_same_bits(load(tmp_path, "w_sgd.bin", np.float32), w2, "standalone SGD w")
+    assert_same_bits(load(tmp_path, "v_sgd.bin", np.float32), v2, "standalone SGD v")
+
+
 @pytest.mark.parametrize("fp16", [False, True])
 def test_c_client_dense(client, tmp_path, fp16):
     wl = workloads.custom(5, [1000, 37, 4099], fp16, sigma=1e-2, scale_mode="layer")
@@ -64,6 +82,7 @@ def test_c_client_dense(client, tmp_path, fp16):
     assert_same_bits(load(tmp_path, "gbar.bin", np.float32), g, "gbar")
     assert_same_bits(load(tmp_path, "w_out.bin", np.float32), w, "w")
     assert_same_bits(load(tmp_path, "v_out.bin", np.float32), v, "v")
+    check_pack_and_sgd(tmp_path, wl, ld, buckets[0], g, w, v)
 
 
 def test_c_client_sparse(client, tmp_path):
@@ -84,3 +103,4 @@ def test_c_client_sparse(client, tmp_path):
     assert_same_bits(load(tmp_path, "gbar.bin", np.float32), res.gbar, "gbar")
     assert_same_bits(load(tmp_path, "w_out.bin", np.float32), w, "w")
     assert_same_bits(load(tmp_path, "v_out.bin", np.float32), v, "v")
+    check_pack_and_sgd(tmp_path, wl, ld, buckets[0], res.gbar, w, v)
