@@ -35,8 +35,26 @@ def ga():
     return ga
 
 
+_capman = None
+
+
+@pytest.fixture(autouse=True)
+def _progress(request):
+    """Progress lines of these minutes-long tests go to the terminal even while
+    pytest captures output, so that a long test is seen to be running."""
+    global _capman
+    _capman = request.config.pluginmanager.getplugin("capturemanager")
+    yield
+    _capman = None
+
+
 def log(msg):
-    print("[fullsize] %s" % msg, flush=True)
+    line = "[fullsize] %s" % msg
+    if _capman is not None:
+        with _capman.global_and_fixture_disabled():
+            print(line, flush=True)
+    else:
+        print(line, flush=True)
 
 
 @pytest.mark.parametrize("source", ["bucket", "layers"])
@@ -78,15 +96,31 @@ def sent_elements(mask, C, P):
     return np.repeat(((m[:, ch >> 5] >> (ch & 31)) & 1).astype(bool), C, axis=1)[:, :P]
 
 
-def assert_residual(got, r_ref, P, name, lazy_mask=None, C=0):
-    """Every worker's residual, worker by worker; with lazy_mask, the chunks it
-    sets are read as zero (the lazy-zero buffer)."""
-    for w in range(got.shape[0]):
-        r = host(got[w, :P])
+def sent_elements_dev(mask, C, P):
+    """[W][P] bool on the device: the elements of the chunks set in a [W][mw]
+    int32 mask."""
+    n_c = (P + C - 1) // C
+    ch = torch.arange(n_c, device=mask.device)
+    bits = ((mask[:, ch >> 5] >> (ch & 31)) & 1).bool()
+    return bits.repeat_interleave(C, dim=1)[:, :P]
+
+
+def assert_residual(got, ref_dev, P, name, lazy_mask=None, C=0):
+    """Every element of every worker's residual against the oracle's (already
+    on the device), compared on the device 16 workers at a time: bitwise, +0
+    and -0 taken as equal, NaN by position; with lazy_mask, the chunks it sets
+    are read as zero (the lazy-zero buffer)."""
+    W = got.shape[0]
+    for w0 in range(0, W, 16):
+        a = got[w0:w0 + 16, :P]
+        b = ref_dev[w0:w0 + 16, :P]
         if lazy_mask is not None:
-            r = r.copy()
-            r[sent_elements(lazy_mask[w:w + 1], C, P)[0]] = 0.0
-        assert_same_bits(r, r_ref[w, :P], "%s, worker %d" % (name, w))
+            a = torch.where(sent_elements_dev(lazy_mask[w0:w0 + 16], C, P), torch.zeros_like(a), a)
+        same = (a.view(torch.int32) == b.view(torch.int32)) | (a == b) | (torch.isnan(a) & torch.isnan(b))
+        if not bool(same.all()):
+            bad = (~same).nonzero()[0].tolist()
+            raise AssertionError("%s: %d mismatches, first at worker %d element %d: %r vs %r" % (
+                name, int((~same).sum()), w0 + bad[0], bad[1], float(a[bad[0], bad[1]]), float(b[bad[0], bad[1]])))
 
 
 def test_sparse_alexnet128_full_size(ga):
@@ -130,7 +164,9 @@ def test_sparse_alexnet128_full_size(ga):
         assert_close(host(gd), res.gbar, TOL_FP32, "gbar")
         assert_same_bits(host(wd), w_ref, "w")
         assert_same_bits(host(vd), v_ref, "v")
-        assert_residual(rd, r_ref, P, "lazy residual step %d" % step, lazy_mask=host(mask), C=C)
+        ref_dev = torch.from_numpy(r_ref).cuda()
+        assert_residual(rd, ref_dev, P, "lazy residual step %d" % step, lazy_mask=mask, C=C)
+        del ref_dev
         log("step %d compared in %.1fs (total %.1fs)" % (step, time.time() - t1, time.time() - t0))
 
 
@@ -167,12 +203,13 @@ def test_buckets_alexnet16_full_size(ga, cap):
 class DeviceRun:
     """One GPU instance of the deferred step: its residual, state and history."""
 
-    def __init__(self, plan, w_init):
+    def __init__(self, plan, w_init, v_init=None):
         self.plan = plan
         self.rd = plan.empty_residual()
         self.keys = plan.empty_keys()
         self.idx = torch.empty((plan.W, plan.k), dtype=torch.int32, device="cuda")
-        self.wd, self.vd = to_dev(w_init.copy()), torch.zeros(plan.P, dtype=torch.float32, device="cuda")
+        self.wd = to_dev(w_init.copy())
+        self.vd = torch.zeros(plan.P, dtype=torch.float32, device="cuda") if v_init is None else to_dev(v_init)
         self.gd = torch.empty(plan.P, dtype=torch.float32, device="cuda")
         self.masks, self.tables = [None], []
         self.last = None
@@ -198,32 +235,34 @@ class DeviceRun:
         self.plan.residual_flush(ptrs, hist, store, out, sel)
         return out
 
-    def check(self, res, w_ref, v_ref, r_ref, scratch, name):
+    def check(self, res, w_ref, v_ref, ref_dev, scratch, name):
         assert np.array_equal(host(self.idx), res.sel_idx), name + ": selected chunk indices differ"
         assert np.array_equal(host(self.masks[0]).view(np.uint32), res.sel_mask), name + ": mask"
         assert_close(host(self.keys), res.keys, KEY_RTOL, name + ": keys")
         assert_same_bits(host(self.gd), res.gbar, name + ": gbar")
         assert_same_bits(host(self.wd), w_ref, name + ": w")
         assert_same_bits(host(self.vd), v_ref, name + ": v")
-        assert_residual(self.flush(scratch), r_ref, self.plan.P, name + ": flushed residual")
+        assert_residual(self.flush(scratch), ref_dev, self.plan.P, name + ": flushed residual")
 
 
-@pytest.mark.parametrize("depth,steps,resume_after", [(1, 5, 3), (2, 4, None)])
+def _sparse_setup(ga):
+    wl = workloads.WORKLOADS["alexnet128_sparse"]
+    plan = ga.Plan(wl.W, wl.numels, True, chunk=wl.chunk, keep_ratio=wl.rho)
+    return wl, plan, workloads.segments(wl)
+
+
+@pytest.mark.parametrize("depth,steps,resume_after", [(1, 4, 2), (2, 3, None)])
 def test_sparse_alexnet128_full_size_deferred(ga, depth, steps, resume_after):
     """The benchmarked deferred form at full size, every output against the
-    oracle at every step (the residual through a flush into a copy).  With
-    resume_after, a second run beside it is checkpointed after that step:
-    flushed in place, its residual, weights and velocity copied to the host,
-    the device buffers dropped, and resumed from the host copies alone (age 0,
-    no mask, no earlier gradient tensor); it must match the oracle (and so the
-    straight run) at every later step.  At depth 2 one more step is repeated
-    five times from the same saved state and must give bitwise identical
-    keys, masks, mean gradient, weights, velocity and flushed residual."""
-    wl = workloads.WORKLOADS["alexnet128_sparse"]
-    C = wl.chunk
-    plan = ga.Plan(wl.W, wl.numels, True, chunk=C, keep_ratio=wl.rho)
-    P, ld, k = wl.P, plan.ld, plan.k
-    seg = workloads.segments(wl)
+    oracle at every step (the residual of all 128 workers through a flush
+    into a copy).  At depth 1 a second run beside it is checkpointed after
+    step `resume_after`: flushed in place, its residual, weights and velocity
+    copied to the host, its device buffers and history dropped, and resumed
+    from the host copies alone (age 0, no mask, no earlier gradient tensor);
+    it must match the oracle, and so the straight run, at every later step.
+    Depth 2 covers every age (0, 1, 2) in its 3 steps."""
+    wl, plan, seg = _sparse_setup(ga)
+    C, P, ld, k = wl.chunk, wl.P, plan.ld, plan.k
     w_ref = workloads.weights(wl)
     v_ref = np.zeros(P, np.float32)
     r_ref = np.zeros((wl.W, ld), np.float32)
@@ -240,48 +279,62 @@ def test_sparse_alexnet128_full_size_deferred(ga, depth, steps, resume_after):
         res = oracle.sparse_step(b, P, True, C, k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
         del b
         assert np.all(res.margin > 1e-12), "selection boundary too close to certify"
+        ref_dev = torch.from_numpy(r_ref).cuda()
+        log("depth %d step %d: inputs and oracle in %.1fs" % (depth, step, time.time() - t0))
         for name, run in runs.items():
             run.step(ptrs, depth, wl.lr, wl.mu)
             torch.cuda.synchronize()
-            run.check(res, w_ref, v_ref, r_ref, scratch, "depth %d %s step %d" % (depth, name, step))
+            run.check(res, w_ref, v_ref, ref_dev, scratch, "depth %d %s step %d" % (depth, name, step))
+        del ref_dev
         if resume_after and step == resume_after:
-            old = runs["resumed"]
+            old = runs.pop("resumed")
             old.flush(old.rd)
             torch.cuda.synchronize()
-            saved = (host(old.rd).copy(), host(old.wd).copy(), host(old.vd).copy())
-            del runs["resumed"], old
+            saved = (host(old.rd), host(old.wd), host(old.vd))
+            del old
             torch.cuda.empty_cache()
-            new = DeviceRun(plan, saved[1])
+            new = DeviceRun(plan, saved[1], saved[2])
             new.rd.copy_(torch.from_numpy(saved[0]))
-            new.vd.copy_(torch.from_numpy(saved[2]))
             del saved
             runs["resumed"] = new          # age 0, no mask, no earlier tensor
             log("depth %d: checkpoint after step %d, resumed from the host copy" % (depth, step))
         log("depth %d step %d compared in %.1fs" % (depth, step, time.time() - t0))
-    if depth == 2:
-        # determinism: the next step five times from one saved state
-        run = runs["straight"]
-        b = workloads.grad_bucket(wl, steps + 1, ld, seg=seg)
+
+
+def test_sparse_alexnet128_deferred_deterministic(ga):
+    """The benchmarked step at full size (depth 2, so that every earlier-step
+    table and mask is in play) repeated five times from one saved state: keys,
+    masks, mean gradient, weights, velocity and the flushed residual are
+    bitwise identical every time."""
+    wl, plan, seg = _sparse_setup(ga)
+    P, ld, depth = wl.P, plan.ld, 2
+    run = DeviceRun(plan, workloads.weights(wl))
+    scratch = plan.empty_residual()
+    kept, ptrs = [], None
+    for step in range(1, 4):
+        b = workloads.grad_bucket(wl, step, ld, seg=seg)
         buf, ptrs = device_layers(b[:, :P], wl.numels)
         del b
         kept = (kept + [buf])[-(depth + 1):]
-        state = (run.rd.clone(), run.wd.clone(), run.vd.clone(), list(run.masks), list(run.tables))
-        outs = []
-        for rep in range(5):
-            run.rd.copy_(state[0])
-            run.wd.copy_(state[1])
-            run.vd.copy_(state[2])
-            run.masks, run.tables = list(state[3]), list(state[4])
+        if step < 3:
             run.step(ptrs, depth, wl.lr, wl.mu)
-            got = [run.keys.clone(), run.masks[0].clone(), run.gd.clone(), run.wd.clone(), run.vd.clone()]
-            run.flush(scratch)
-            torch.cuda.synchronize()
-            if rep == 0:
-                outs = got
-                first_r = scratch.clone()
-            else:
-                for a, b_ in zip(outs, got):
-                    assert torch.equal(a.view(torch.int32) if a.dtype != torch.float64 else a.view(torch.int64),
-                                       b_.view(torch.int32) if b_.dtype != torch.float64 else b_.view(torch.int64))
-                assert torch.equal(scratch.view(torch.int32), first_r.view(torch.int32))
-        log("depth 2: step %d repeated 5 times, bitwise identical" % (steps + 1))
+        log("deterministic: step %d ready" % step)
+    state = (run.rd.clone(), run.wd.clone(), run.vd.clone(), list(run.masks), list(run.tables))
+    first = None
+    for rep in range(5):
+        run.rd.copy_(state[0])
+        run.wd.copy_(state[1])
+        run.vd.copy_(state[2])
+        run.masks, run.tables = list(state[3]), list(state[4])
+        run.step(ptrs, depth, wl.lr, wl.mu)
+        out = [run.keys.view(torch.int64).clone(), run.masks[0].clone(), run.gd.view(torch.int32).clone(),
+               run.wd.view(torch.int32).clone(), run.vd.view(torch.int32).clone()]
+        run.flush(scratch)
+        torch.cuda.synchronize()
+        if first is None:
+            first, first_r = out, scratch.clone()
+        else:
+            for name, a, b in zip(("keys", "mask", "gbar", "w", "v"), first, out):
+                assert torch.equal(a, b), "repetition %d: %s differs" % (rep, name)
+            assert torch.equal(scratch.view(torch.int32), first_r.view(torch.int32)), "repetition %d: residual" % rep
+        log("deterministic: repetition %d done" % rep)
