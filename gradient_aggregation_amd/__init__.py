@@ -25,6 +25,7 @@ ORDERS = {"tree": 0, "server": 1, "ring": 2}
 MAX_WORKERS = 1024
 MAX_CHUNKS = 65536
 MAX_ELEMENTS = 1 << 33
+STATIC_KEYS = 1 << 20
 
 
 class GAError(RuntimeError):
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.ga_chunk_topk.argtypes = [_VP, _VP, _VP, _VP, _VP]
         L.ga_chunk_norm_topk.restype = st
         L.ga_chunk_norm_topk.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.ga_chunk_norm_topk_static.restype = st
+        L.ga_chunk_norm_topk_static.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP]
         L.ga_sparse_gather_reduce.restype = st
         L.ga_sparse_gather_reduce.argtypes = [_VP, _VP, _VP, ctypes.c_int32, _VP, ctypes.POINTER(SGD), _VP, _VP,
                                               _VP]
@@ -388,6 +391,17 @@ class Plan:
             _dev(resid, torch.float32, self.W * self.ld, "resid"),
             _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
             _dev(keys, torch.float64, self.W * self.n_chunks, "keys"),
+            _dev(sel_idx, torch.int32, self.W * self.k, "sel_idx"),
+            _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
+
+    def chunk_norm_topk_static(self, bucket, resid, sel_idx, sel_mask, prev_mask=None) -> None:
+        """chunk_norm_topk with the keys in the library's fixed array (no
+        allocation; concurrent calls on one device race)."""
+        torch = _torch()
+        _check(lib().ga_chunk_norm_topk_static(
+            self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),
+            _dev(resid, torch.float32, self.W * self.ld, "resid"),
+            _dev(prev_mask, torch.int32, self.W * self.mask_words, "prev_mask"),
             _dev(sel_idx, torch.int32, self.W * self.k, "sel_idx"),
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
 

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgradagg.so")
-SOURCES = ["abi.hip", "buckets.hip", "dense.hip", "variants.hip", "norm.hip", "topk.hip", "gather.hip", "history.hip", "pack.hip"]
+SOURCES = ["abi.hip", "buckets.hip", "dense.hip", "variants.hip", "norm.hip", "topk.hip", "gather.hip", "history.hip", "noalloc.hip", "pack.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

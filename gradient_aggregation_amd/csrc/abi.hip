@@ -105,6 +105,12 @@ ga_status check_device(const ga::Plan* p) {
 }  // namespace
 
 namespace ga {
+// The fixed key array of ga_chunk_norm_topk_static (noalloc.hip): look up its
+// address on `device` (which must be current) once; then static_keys(device)
+// returns it (nullptr before, or if the lookup failed).
+hipError_t static_keys_setup(int device);
+double* static_keys(int device);
+
 // Record a failure message for ga_last_error (used by the other ABI sources).
 ga_status api_fail(ga_status s, const char* msg) { return fail(s, "%s", msg); }
 ga_status api_ok() { return ok(); }
@@ -202,6 +208,10 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
         delete p;
         return device_status(e, "plan device table");
     }
+    // the fixed key array of ga_chunk_norm_topk_static: its address on this
+    // device, looked up once per device (a failure shows as GA_ERR_DEVICE from
+    // that call only)
+    (void)ga::static_keys_setup(p->device);
     *out = reinterpret_cast<ga_plan*>(p);
     return ok();
 }
@@ -415,6 +425,29 @@ ga_status ga_chunk_norm_topk(const ga_plan* plan, const void* d_bucket, float* d
     ga_status st = ga_chunk_norm(plan, d_bucket, d_residual, d_prev_mask, d_keys, stream);
     if (st != GA_OK) return st;
     return ga_chunk_topk(plan, d_keys, d_sel_idx, d_sel_mask, stream);
+}
+
+ga_status ga_chunk_norm_topk_static(const ga_plan* plan, const void* d_bucket, float* d_residual,
+                                    const uint32_t* d_prev_mask, int32_t* d_sel_idx, uint32_t* d_sel_mask,
+                                    hipStream_t stream) {
+    if (!plan || !d_bucket || !d_residual || !d_sel_mask) return fail(GA_ERR_INVALID, "NULL argument");
+    const ga::Plan* p = as_plan(plan);
+    if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
+    if (p->k > 0 && !d_sel_idx) return fail(GA_ERR_INVALID, "sel_idx is NULL with k > 0");
+    if ((int64_t)p->W * p->n_c > GA_STATIC_KEYS)
+        return fail(GA_ERR_UNSUPPORTED, "W * n_c = %lld keys exceed the %lld of the fixed array",
+                    (long long)p->W * p->n_c, (long long)GA_STATIC_KEYS);
+    if (!aligned16(d_bucket) || !aligned16(d_residual) || (d_prev_mask && ((uintptr_t)d_prev_mask & 3u)) ||
+        ((uintptr_t)d_sel_mask & 3u) || (d_sel_idx && ((uintptr_t)d_sel_idx & 3u)))
+        return fail(GA_ERR_ALIGN, "misaligned device buffer");
+    ga_status st = check_device(p);
+    if (st != GA_OK) return st;
+    double* keys = ga::static_keys(p->device);
+    if (!keys) return fail(GA_ERR_DEVICE, "the fixed key array has no address on device %d", p->device);
+    st = device_status(ga::launch_chunk_norm(*p, d_bucket, d_residual, d_prev_mask, keys, stream),
+                       "chunk_norm_topk_static launch");
+    if (st != GA_OK) return st;
+    return device_status(ga::launch_topk(*p, keys, d_sel_idx, d_sel_mask, stream), "chunk_norm_topk_static launch");
 }
 
 ga_status ga_sparse_gather_reduce(const ga_plan* plan, float* d_residual, const uint32_t* d_sel_mask,

@@ -240,6 +240,27 @@ ga_status ga_chunk_norm_topk(const ga_plan* plan, const void* d_bucket, float* d
                              uint32_t* d_sel_mask, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as ga_chunk_norm_topk, with the [W][n_c] binary64 keys held in a
+ * fixed array inside the library instead of a caller buffer.  The array holds
+ * GA_STATIC_KEYS keys (8 MiB) on every device the library runs on, until the
+ * process ends; its address on a device is looked up when a plan is created
+ * there.  The call allocates nothing and calls no allocating routine.
+ * Every call on one device uses the same array, so calls that overlap on one
+ * device (other streams, other threads) race; each call overwrites every key
+ * it reads, so nothing needs clearing between calls.  Results equal
+ * ga_chunk_norm_topk's bit for bit.
+ * Errors: those of ga_chunk_norm_topk (d_keys aside); GA_ERR_UNSUPPORTED when
+ * W * n_c > GA_STATIC_KEYS; GA_ERR_DEVICE when the array's address could not
+ * be looked up on the plan's device.
+ */
+#define GA_STATIC_KEYS ((int64_t)1 << 20)
+ga_status ga_chunk_norm_topk_static(const ga_plan* plan, const void* d_bucket, float* d_residual,
+                                    const uint32_t* d_prev_mask, int32_t* d_sel_idx, uint32_t* d_sel_mask,
+                                    hipStream_t stream);
+
+/*
  * Part 3: sum what the workers send.  Worker w sends t[w][i] = a[w][i] on its
  * selected chunks and nothing elsewhere; absent values enter the same fixed
  * tree as +0 (binary32 throughout, so residual + sent == a exactly):
