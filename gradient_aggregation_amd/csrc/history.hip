@@ -57,14 +57,17 @@ __device__ __forceinline__ bool mask_bit(const uint32_t* __restrict__ m, int64_t
     return (m[w * mw + (c >> 5)] >> (c & 31)) & 1u;
 }
 
-// Eight gradient elements at element j of tensor src (16-byte aligned there), widened.
+// Eight gradient elements at element j of tensor src (16-byte aligned there),
+// widened, by non-temporal loads (streamed once, not kept in the caches).
 template <bool FP16>
-__device__ __forceinline__ void load8(gptr<void> src, int64_t j, float (&f)[8]) {
+__device__ __forceinline__ void load8_nt(gptr<void> src, int64_t j, float (&f)[8]) {
     if (FP16) {
-        widen8(load_u4(static_cast<gptr<uint16_t>>(src) + j), f);
+        const u32x4 x =
+            __builtin_nontemporal_load(reinterpret_cast<gptr<u32x4>>(static_cast<gptr<uint16_t>>(src) + j));
+        widen8(make_uint4(x.x, x.y, x.z, x.w), f);
     } else {
-        gptr<float> gp = static_cast<gptr<float>>(src) + j;
-        const float4 g0 = load_f4(gp), g1 = load_f4(gp + 4);
+        gptr<f32x4> gp = reinterpret_cast<gptr<f32x4>>(static_cast<gptr<float>>(src) + j);
+        const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
         f[0] = g0.x; f[1] = g0.y; f[2] = g0.z; f[3] = g0.w;
         f[4] = g1.x; f[5] = g1.y; f[6] = g1.z; f[7] = g1.w;
     }
@@ -107,12 +110,15 @@ __device__ __forceinline__ void norm_seg(gptr<void> g0, gptr<void> g1, gptr<void
             const int64_t jj = j + u * kNormThreads;
             if (jj >= nvec) continue;
             const int64_t i = ss + (jj << 3);
-            load8<FP16>(g0, i - soff, x0[u]);
-            if (NP >= 1) load8<FP16>(g1, i - soff, x1[u]);
-            if (NP >= 2) load8<FP16>(g2, i - soff, x2[u]);
+            // Gradients stream with non-temporal loads; so does R when it is
+            // only read.  (Where R is also written here, non-temporal reads of
+            // it measured slower.)
+            load8_nt<FP16>(g0, i - soff, x0[u]);
+            if (NP >= 1) load8_nt<FP16>(g1, i - soff, x1[u]);
+            if (NP >= 2) load8_nt<FP16>(g2, i - soff, x2[u]);
             if (BUF) {
-                const float4 r0 = *reinterpret_cast<const float4*>(r + i);
-                const float4 r1 = *reinterpret_cast<const float4*>(r + i + 4);
+                const float4 r0 = ST ? *reinterpret_cast<const float4*>(r + i) : load_f4_nt(r + i);
+                const float4 r1 = ST ? *reinterpret_cast<const float4*>(r + i + 4) : load_f4_nt(r + i + 4);
                 rb[u][0] = r0.x; rb[u][1] = r0.y; rb[u][2] = r0.z; rb[u][3] = r0.w;
                 rb[u][4] = r1.x; rb[u][5] = r1.y; rb[u][6] = r1.z; rb[u][7] = r1.w;
             }
