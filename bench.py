@@ -83,6 +83,10 @@ def parse():
                     help="--overlap: bucket thresholds to compare, MiB per worker")
     ap.add_argument("--reduce-workgroups", default="0,512",
                     help="--overlap: grid caps of the bucket reductions to compare (0: full grid)")
+    ap.add_argument("--cu-split", default="",
+                    help="--overlap: also run the overlapped schedule with the compute units partitioned: the "
+                         "reductions on a stream confined to CUs 0..N-1, the producer on a stream with the others "
+                         "(comma-separated multiples of 32)")
     ap.add_argument("--producer", choices=["gemm", "dense", "copy"], default="gemm",
                     help="--overlap: each layer's gradients come from its weight-gradient GEMM (gemm), from "
                          "the same flops as square 4096^3 GEMMs plus a copy of a staged gradient (dense), or "
@@ -594,6 +598,37 @@ def run_overlap(args):
     import torch
     import gradient_aggregation_amd as ga
     import workloads
+    # CU-partitioned stream pairs for --cu-split, made before anything else
+    # runs: for N in the list (a multiple of 32), one stream confined to CUs
+    # 0 .. N-1 and one to the others.  (On the runtime used here a mask that
+    # spreads the CUs over the chip, every 16th, was refused with error 2.)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    hip = None
+    cu_streams = {}
+    if args.cu_split:
+        import ctypes
+        # the HIP runtime this process already uses (torch's copy): a second
+        # copy loaded by name would be a separate runtime
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        hip = ctypes.CDLL(path)
+        words = (n_cu + 31) // 32
+        for ncu in [int(x) for x in args.cu_split.split(",") if x]:
+            if ncu % 32 or not 0 < ncu < n_cu:
+                raise ValueError("--cu-split values must be multiples of 32 below %d" % n_cu)
+            red_set = set(range(ncu))
+            pair = []
+            for want in (True, False):
+                m = (ctypes.c_uint32 * words)()
+                for c in range(n_cu):
+                    if (c in red_set) == want:
+                        m[c >> 5] |= 1 << (c & 31)
+                h = ctypes.c_void_p()
+                rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), m)
+                if rc != 0:
+                    raise RuntimeError("hipExtStreamCreateWithCUMask(%d CUs) returned %d" % (
+                        len(red_set) if want else n_cu - len(red_set), rc))
+                pair.append(h)
+            cu_streams[ncu] = (red_set, pair)
     wl = workloads.WORKLOADS[args.workload if args.workload != "alexnet128_sparse" else "alexnet16"]
     if wl.mode != "dense":
         print("--overlap applies to the dense workloads", file=sys.stderr)
@@ -727,7 +762,63 @@ def run_overlap(args):
             log("bucket %g MiB (%d buckets), grid cap %d: T_prod %.3f, T_red %.3f (buckets %.3f), T_serial %.3f, "
                 "T_overlap %.3f ms; hidden %.3f ms; efficiency %.2f" % (
                     mb, bk.count, cap, t_prod, t_red, t_bk, t_serial, t_ov, t_prod + t_red - t_ov, eff))
+        for ncu in [int(x) for x in args.cu_split.split(",") if x]:
+            # partitioned compute units: the reductions on CUs 0 .. ncu-1,
+            # the producer on the rest
+            red_set, streams = cu_streams[ncu]
+            m_red, m_prod = (torch.cuda.ExternalStream(h.value) for h in streams)
+
+            def overlapped_cu():
+                start_ev.record(main)
+                m_prod.wait_event(start_ev)
+                m_red.wait_event(start_ev)
+                with torch.cuda.stream(m_prod):
+                    for l in range(L - 1, -1, -1):
+                        produce(l)
+                        if l in first_to_bucket:
+                            ready[first_to_bucket[l]].record(m_prod)
+                    done_p.record(m_prod)
+                with torch.cuda.stream(m_red):
+                    for b in range(bk.count):
+                        bk.reduce_layers(b, ptrs, ready[b], None, wd, vd, lr, mu)
+                    done_r.record(m_red)
+                main.wait_event(done_p)
+                main.wait_event(done_r)
+
+            def prod_part():
+                start_ev.record(main)
+                m_prod.wait_event(start_ev)
+                with torch.cuda.stream(m_prod):
+                    prod_all()
+                    done_p.record(m_prod)
+                main.wait_event(done_p)
+
+            def red_part():
+                start_ev.record(main)
+                m_red.wait_event(start_ev)
+                with torch.cuda.stream(m_red):
+                    for b in range(bk.count):
+                        bk.reduce_layers(b, ptrs, None, None, wd, vd, lr, mu)
+                    done_r.record(m_red)
+                main.wait_event(done_r)
+
+            t_prod, t_red, t_pp, t_rp, t_serial, t_ov = timed_interleaved(
+                [prod_all, red_all, prod_part, red_part, serial, overlapped_cu], reps)
+            eff = (t_serial - t_ov) / min(t_prod, t_red)
+            rows.append({"bucket_mib": mb, "buckets": bk.count, "cu_split": ncu, "reduction_cus": len(red_set),
+                         "T_prod_ms": round(t_prod, 4), "T_red_ms": round(t_red, 4),
+                         "T_prod_on_rest_ms": round(t_pp, 4), "T_red_on_split_ms": round(t_rp, 4),
+                         "T_serial_ms": round(t_serial, 4), "T_overlap_ms": round(t_ov, 4),
+                         "hidden_ms": round(t_prod + t_red - t_ov, 4), "efficiency": round(eff, 3)})
+            log("bucket %g MiB (%d buckets), reductions on %d CUs: T_prod %.3f (on the rest %.3f), T_red %.3f "
+                "(on %d CUs %.3f), T_serial %.3f, T_overlap %.3f ms; efficiency %.2f" % (
+                    mb, bk.count, len(red_set), t_prod, t_pp, t_red, len(red_set), t_rp, t_serial, t_ov, eff))
+            torch.cuda.synchronize()
+            del m_red, m_prod
         bk.close()
+    for _, streams in cu_streams.values():
+        for h in streams:
+            hip.hipStreamDestroy(h)
     best = max(rows, key=lambda r: r["efficiency"])
     b_alg = W * P * esz + 16 * P
     result = {
