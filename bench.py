@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--residual", choices=["deferred", "lazy"], default="deferred",
                     help="sparse workload: the deferred residual (written every depth+1 steps, re-formed from the "
                          "held gradients in between) or the lazy-zero sequence of the boundary's calls")
-    ap.add_argument("--depth", type=int, default=1,
+    ap.add_argument("--depth", type=int, default=2,
                     help="deferred residual: earlier gradient batches held (the residual is stored every depth+1 "
                          "steps)")
     ap.add_argument("--order", choices=["tree", "server", "ring"], default="tree",

@@ -251,16 +251,17 @@ def _sparse_setup(ga):
     return wl, plan, workloads.segments(wl)
 
 
-@pytest.mark.parametrize("depth,steps,resume_after", [(1, 4, 2), (2, 3, None)])
+@pytest.mark.parametrize("depth,steps,resume_after", [(2, 4, 2), (1, 3, 1)])
 def test_sparse_alexnet128_full_size_deferred(ga, depth, steps, resume_after):
-    """The benchmarked deferred form at full size, every output against the
-    oracle at every step (the residual of all 128 workers through a flush
-    into a copy).  At depth 1 a second run beside it is checkpointed after
-    step `resume_after`: flushed in place, its residual, weights and velocity
-    copied to the host, its device buffers and history dropped, and resumed
-    from the host copies alone (age 0, no mask, no earlier gradient tensor);
-    it must match the oracle, and so the straight run, at every later step.
-    Depth 2 covers every age (0, 1, 2) in its 3 steps."""
+    """The deferred form at full size (depth 2 as benchmarked, and depth 1),
+    every output against the oracle at every step (the residual of all 128
+    workers through a flush into a copy).  A second run beside the straight
+    one is checkpointed after step `resume_after`, a step that did not store
+    the residual: flushed in place, its residual, weights and velocity copied
+    to the host, its device buffers and history dropped, and resumed from the
+    host copies alone (age 0, no mask, no earlier gradient tensor); it must
+    match the oracle, and so the straight run, at every later step.  The
+    straight run at depth 2 passes every age (0, 1, 2, then 0 again)."""
     wl, plan, seg = _sparse_setup(ga)
     C, P, ld, k = wl.chunk, wl.P, plan.ld, plan.k
     w_ref = workloads.weights(wl)
