@@ -29,7 +29,10 @@ hipError_t static_keys_setup(int device) {
     if (g_ptr[device]) return hipSuccess;
     void* p = nullptr;
     const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+        (void)hipGetLastError();   // not to be reported by the next launch check
+        return e;
+    }
     g_ptr[device] = static_cast<double*>(p);
     return hipSuccess;
 }

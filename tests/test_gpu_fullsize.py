@@ -304,7 +304,7 @@ def test_sparse_alexnet128_full_size_deferred(ga, depth, steps, resume_after):
 
 def test_sparse_alexnet128_deferred_deterministic(ga):
     """The benchmarked step at full size (depth 2, so that every earlier-step
-    table and mask is in play) repeated five times from one saved state: keys,
+    table and mask is in play) repeated ten times from one saved state: keys,
     masks, mean gradient, weights, velocity and the flushed residual are
     bitwise identical every time."""
     wl, plan, seg = _sparse_setup(ga)
@@ -322,7 +322,7 @@ def test_sparse_alexnet128_deferred_deterministic(ga):
         log("deterministic: step %d ready" % step)
     state = (run.rd.clone(), run.wd.clone(), run.vd.clone(), list(run.masks), list(run.tables))
     first = None
-    for rep in range(5):
+    for rep in range(10):
         run.rd.copy_(state[0])
         run.wd.copy_(state[1])
         run.vd.copy_(state[2])
