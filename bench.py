@@ -563,13 +563,18 @@ def main():
             log("lazy-zero sequence: %.3f ms/step" % lms)
             del lstep, lholder
         log("protocol: %s" % {k: v["step_ms_median"] for k, v in result["protocol"].items()})
+    if args.cpu_baseline:
+        result["cpu_baseline"], ostate = cpu_baseline(wl, plan, host_first, w_init, thr)
+        del host_first
+        if not variant:
+            result["parity_full_size"] = full_size_parity(
+                plan, wl, sources[0], w_init, "deferred" if deferred else "lazy", args.depth, layers_src, ostate)
+            log("full-size parity: %s" % result["parity_full_size"])
+        del ostate
     if args.extras:
         del sources, keep, states
         torch.cuda.empty_cache()
         result["dense_workloads"] = dense_summary(thr)
-
-    if args.cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, plan, host_first, w_init, thr)
     print(json.dumps(result), flush=True)
 
 
@@ -971,7 +976,8 @@ def cpu_baseline(wl, plan, host_bucket, w_init, thr, min_s=10.0, max_steps=5):
     """The oracle, as it is, timed on the host cores: whole steps of the
     workload (all W workers) on the first gradient batch, repeated until at
     least `min_s` seconds of work (at most `max_steps` steps); the sparse
-    residual and the w, v state carry over from step to step."""
+    residual and the w, v state carry over from step to step.  Returns the
+    record and the oracle's final state (steps, w, v, residual or None)."""
     import oracle
     P = wl.P
     b_in = 2 if wl.fp16 else 4
@@ -991,7 +997,6 @@ def cpu_baseline(wl, plan, host_bucket, w_init, thr, min_s=10.0, max_steps=5):
         if time.time() - t0 >= min_s or steps >= max_steps:
             break
     total = time.time() - t0
-    del r
     t = total / steps
     b_alg = wl.W * P * ((b_in + 8) if sparse else b_in) + 16 * P
     log("cpu baseline: %d oracle steps over all %d workers in %.2fs on %d threads" % (steps, wl.W, total, thr))
@@ -1004,11 +1009,71 @@ def cpu_baseline(wl, plan, host_bucket, w_init, thr, min_s=10.0, max_steps=5):
                     break
     except OSError:
         pass
-    return {"value": round(b_alg / t / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
-            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
-            "sample": "%d consecutive whole %s steps of the workload (all %d workers, P=%d) on the first "
-                      "gradient batch, oracle threads=%d, %.2f s in all, %.2f s per step"
-                      % (steps, wl.mode, wl.W, P, thr, total, t)}
+    rec = {"value": round(b_alg / t / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
+           "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+           "sample": "%d consecutive whole %s steps of the workload (all %d workers, P=%d) on the first "
+                     "gradient batch, oracle threads=%d, %.2f s in all, %.2f s per step"
+                     % (steps, wl.mode, wl.W, P, thr, total, t)}
+    return rec, (steps, w, v, r)
+
+
+def full_size_parity(plan, wl, src0, w_init, mode, depth, layers_src, ostate):
+    """The timed path run on the first gradient batch for as many steps as the
+    oracle ran in cpu_baseline, from the same initial state, and compared with
+    the oracle's final w, v and residual (every worker, every element, on the
+    device one worker row at a time).  The deferred form gets one layer table
+    per step (copies of the first batch's table: the same tensors, unchanged,
+    as its history requires) and is flushed; in the lazy-zero form the chunks
+    of the last mask are +0.  Bit patterns are compared; +0 against -0 would
+    show as a difference."""
+    import torch
+    steps, w_ref, v_ref, r_ref = ostate
+    P, W = wl.P, wl.W
+    wd = torch.from_numpy(w_init).cuda()
+    vd = torch.zeros(P, dtype=torch.float32, device="cuda")
+    if r_ref is None:
+        for _ in range(steps):
+            if layers_src:
+                plan.tree_reduce_layers(src0, None, wd, vd, wl.lr, wl.mu)
+            else:
+                plan.tree_reduce(src0, None, wd, vd, wl.lr, wl.mu)
+        resid, mask = None, None
+    else:
+        srcs = [src0.clone() for _ in range(steps)] if layers_src else [src0] * steps
+        step, holder = sparse_stepper(plan, wl, srcs, (wd, vd), mode, depth, layers_src)
+        ev = [torch.cuda.Event() for _ in range(3)]
+        for t in range(steps):
+            step(t, ev)
+        if mode == "deferred":
+            resid, mask = holder.flush(), None
+        else:
+            resid, mask = holder.resid, holder.mask
+    torch.cuda.synchronize()
+
+    def same(a, ref):
+        return torch.equal(a.view(torch.int32), torch.from_numpy(ref).cuda().view(torch.int32))
+
+    out = {"steps": steps, "form": ("deferred, depth %d" % depth) if mode == "deferred" and r_ref is not None
+           else ("lazy-zero" if r_ref is not None else "dense tree"),
+           "against": "the oracle's state after the cpu_baseline steps",
+           "w": "bitwise" if same(wd, w_ref) else "differs",
+           "v": "bitwise" if same(vd, v_ref) else "differs"}
+    if r_ref is not None:
+        C = plan.chunk
+        cid = torch.arange(P, device="cuda") // C
+        bad = 0
+        for wk in range(W):
+            row = resid[wk, :P]
+            if mask is not None:
+                bits = (mask[wk][cid >> 5] >> (cid & 31)) & 1
+                row = torch.where(bits.bool(), torch.zeros_like(row), row)
+            ref = torch.from_numpy(r_ref[wk, :P]).cuda()
+            bad += int((row.view(torch.int32) != ref.view(torch.int32)).sum())
+        out["residual"] = "bitwise, all %d workers" % W if bad == 0 else "%d elements differ" % bad
+        del cid, holder, step, srcs
+    del wd, vd, resid
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
