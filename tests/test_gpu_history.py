@@ -128,6 +128,17 @@ def test_history_matches_oracle(ga, period, fp16, W, numels, C, mis):
     assert stores == [(t % period) == 0 for t in range(1, 7)]
 
 
+@pytest.mark.parametrize("fp16,mis", [(True, "mixed"), (False, "aligned")])
+def test_history_maximum_worker_count(ga, fp16, mis):
+    """W at the library's limit (1024 workers: eleven tree levels, and the
+    groups' bitmaps reloaded per group rather than kept), stored every third
+    step so that every age (0, 1, 2) runs."""
+    wl = workloads.custom(ga.MAX_WORKERS, [3000, 77, 1100], fp16, sigma=1e-3, scale_mode="chunk",
+                          scale_log10=(-4.0, 0.0), chunk=256, rho=0.25)
+    stores = run_history(ga, wl, every(3), mis, steps=5)
+    assert stores == [False, False, True, False, False]
+
+
 @pytest.mark.parametrize("seed", [1, 2, 3, 4])
 @pytest.mark.parametrize("fp16", [False, True])
 def test_history_random_schedule(ga, seed, fp16):
