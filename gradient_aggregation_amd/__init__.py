@@ -423,9 +423,11 @@ class DeferredResidual:
     depth+1 steps, the other steps re-form the residual from the held layer
     tables and masks.  The caller passes each step's layer table and keeps its
     tensors unchanged while they are in the history (the next `depth` steps).
-    The residual starts at zero, described by an all-ones mask (every chunk
-    "sent" before the first step), so the buffer is not read until written.
-    depth = 0 is the lazy-zero form."""
+    Without `resid` the residual starts at zero, described by an all-ones mask
+    (every chunk "sent" before the first step), so the buffer is not read
+    until written; a given `resid` (a flushed residual, say from a checkpoint)
+    is the starting residual itself, read at age 0.  depth = 0 is the
+    lazy-zero form."""
 
     def __init__(self, plan: Plan, depth: int, resid=None):
         torch = _torch()
@@ -442,10 +444,13 @@ class DeferredResidual:
             word = (1 << min(32, plan.n_chunks - 32 * q)) - 1
             words.append(word - (1 << 32) if word >= (1 << 31) else word)
         self.all_sent = torch.tensor(words, dtype=torch.int32).repeat(W, 1).cuda()
-        self.hist_masks = [self.all_sent]   # masks[j]: step t-1-j
+        # masks[j]: step t-1-j; None at age 0: the buffer holds the residual
+        self.hist_masks = [self.all_sent] if resid is None else [None]
         self.hist_tables = []               # layer tables of steps t-1, t-2, ...
         self.next = 0                       # mask buffer the next top-k writes
-        self.last = None                    # (hist, stored, layer_ptrs, sel) of the last step
+        # (hist, stored, layer_ptrs, sel) of the last step; None while the
+        # residual is the starting one or was flushed in place since
+        self.last = None
 
     @property
     def age(self) -> int:
@@ -478,11 +483,24 @@ class DeferredResidual:
 
     def flush(self, out=None):
         """Write the residual after the last step into `out` (default: the live
-        buffer, after which the history restarts at age 0 with no mask)."""
+        buffer, after which the history restarts at age 0 with no mask, so a
+        second flush changes nothing).  Before any step it is the starting
+        residual: zero, or the given one."""
+        if self.last is None:
+            zero_start = self.hist_masks[0] is not None
+            target = self.resid if out is None else out
+            if zero_start:
+                target.zero_()
+            elif target.data_ptr() != self.resid.data_ptr():
+                target.copy_(self.resid)
+            if out is None:
+                self.hist_masks, self.hist_tables = [None], []
+            return target
         hist, stored, layer_ptrs, sel = self.last
         if out is None:
             self.plan.residual_flush(layer_ptrs, hist, stored, self.resid, sel)
             self.hist_masks, self.hist_tables = [None], []
+            self.last = None
             return self.resid
         if out.data_ptr() != self.resid.data_ptr():
             out.copy_(self.resid)

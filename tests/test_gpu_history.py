@@ -214,6 +214,49 @@ def test_deferred_residual_helper(ga, depth):
     plan.close()
 
 
+@pytest.mark.parametrize("depth", [1, 2])
+def test_deferred_residual_helper_resume_and_flush(ga, depth):
+    """The helper's checkpoint path: a flush before any step is the starting
+    residual (zero, or the one given); a second flush in place changes
+    nothing; a helper built on a flushed residual (resid=) continues exactly
+    as the oracle does, with no earlier gradient tensor."""
+    wl = workloads.custom(20, [4096, 5, 3000], True, sigma=1e-3, scale_mode="chunk", scale_log10=(-4.0, 0.0),
+                          chunk=256, rho=0.25)
+    P, W = wl.P, wl.W
+    plan = ga.Plan(W, wl.numels, True, chunk=wl.chunk, keep_ratio=wl.rho)
+    dr = ga.DeferredResidual(plan, depth)
+    dr.resid.fill_(float("nan"))
+    assert torch.count_nonzero(dr.flush(torch.empty_like(dr.resid))).item() == 0
+    w_ref, v_ref = workloads.weights(wl), np.zeros(P, np.float32)
+    r_ref = np.zeros((W, plan.ld), np.float32)
+    wd, vd = to_dev(w_ref.copy()), to_dev(v_ref.copy())
+    gd = torch.empty(P, dtype=torch.float32, device="cuda")
+    kept = []
+    for t in range(1, 7):
+        b = workloads.grad_bucket(wl, t, plan.ld)
+        res = oracle.sparse_step(b, P, True, wl.chunk, plan.k, r_ref, wl.lr, wl.mu, w_ref, v_ref)
+        buf, ptrs = device_layers(b[:, :P], wl.numels, lambda w, l: (w + 2 * l + t) % 4)
+        kept = (kept + [buf])[-(depth + 1):]
+        dr.step(ptrs, gd, wd, vd, wl.lr, wl.mu)
+        torch.cuda.synchronize()
+        assert_same_bits(host(gd), res.gbar, "gbar step %d" % t)
+        assert_same_bits(host(wd), w_ref, "w step %d" % t)
+        if t == depth:                               # a step that did not store
+            assert dr.age > 0
+            saved = dr.flush().clone()
+            again = dr.flush().clone()               # nothing left to add
+            torch.cuda.synchronize()
+            assert_same_bits(host(saved)[:, :P], r_ref[:, :P], "flushed residual")
+            assert torch.equal(saved.view(torch.int32), again.view(torch.int32))
+            # resume: a new helper on the saved residual alone
+            dr = ga.DeferredResidual(plan, depth, resid=saved)
+            assert torch.equal(dr.flush(torch.empty_like(saved)).view(torch.int32), saved.view(torch.int32))
+            kept = []
+    torch.cuda.synchronize()
+    assert_same_bits(host(dr.flush(torch.empty_like(dr.resid)))[:, :P], r_ref[:, :P], "residual at the end")
+    plan.close()
+
+
 def test_history_errors(ga):
     plan = ga.Plan(4, [1000], True, chunk=256, keep_ratio=0.5)
     W, mw = 4, plan.mask_words
