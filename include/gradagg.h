@@ -357,7 +357,10 @@ ga_status ga_sparse_gather_reduce_deferred(const ga_plan* plan, const uint64_t* 
  * else re-formed from the history).  Arguments as given to the step's gather.
  * Afterwards d_residual is the whole residual (for a checkpoint, or before the
  * gradient tensors are reused), and the next step passes age 0 with
- * d_masks[0] = NULL: no earlier tensor or mask is needed to resume.
+ * d_masks[0] = NULL: no earlier tensor or mask is needed to resume.  The
+ * flush reads the buffer as R, so flush in place at most once per step's
+ * history (a second call would add the history again on top of r_t); to keep
+ * the live buffer, flush into a copy of it.
  * Errors as ga_sparse_gather_reduce_deferred (no chunk-size limit).
  */
 ga_status ga_residual_flush(const ga_plan* plan, const uint64_t* d_layer_ptrs, const ga_history* hist,
