@@ -192,6 +192,8 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
     }
     p->d_tile_layer = nullptr;
     p->d_tile_order = nullptr;
+    p->key_parts = p->C > ga::kNormPart ? (int32_t)((p->C + ga::kNormPart - 1) / ga::kNormPart) : 1;
+    p->d_part_keys = nullptr;
     hipError_t e = hipGetDevice(&p->device);
     if (e == hipSuccess) e = hipMalloc((void**)&p->d_offsets, sizeof(int64_t) * (size_t)(n_layers + 1));
     if (e == hipSuccess)
@@ -200,10 +202,14 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
     if (e == hipSuccess)
         e = hipMemcpy(p->d_tile_layer, h_tiles, sizeof(uint32_t) * (size_t)(2 * n_tiles), hipMemcpyHostToDevice);
     if (e == hipSuccess) p->d_tile_order = p->d_tile_layer + n_tiles;
+    if (e == hipSuccess && p->key_parts > 1)
+        e = hipMalloc((void**)&p->d_part_keys,
+                      sizeof(double) * (size_t)W * (size_t)p->n_c * (size_t)p->key_parts);
     free(h_tiles);
     if (e != hipSuccess) {
         if (p->d_offsets) (void)hipFree(p->d_offsets);
         if (p->d_tile_layer) (void)hipFree(p->d_tile_layer);
+        if (p->d_part_keys) (void)hipFree(p->d_part_keys);
         free(p->h_offsets);
         delete p;
         return device_status(e, "plan device table");
@@ -221,6 +227,7 @@ void ga_plan_destroy(ga_plan* plan) {
     ga::Plan* p = reinterpret_cast<ga::Plan*>(plan);
     if (p->d_offsets) (void)hipFree(p->d_offsets);
     if (p->d_tile_layer) (void)hipFree(p->d_tile_layer);
+    if (p->d_part_keys) (void)hipFree(p->d_part_keys);
     free(p->h_offsets);
     delete p;
 }

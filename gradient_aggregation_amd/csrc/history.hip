@@ -154,13 +154,9 @@ __device__ __forceinline__ void norm_seg(gptr<void> g0, gptr<void> g1, gptr<void
 template <bool FP16, int NP, bool BUF, bool ST>
 __device__ __forceinline__ void norm_walk(const HistArgs& h, const int64_t* __restrict__ offsets, int32_t L,
                                           int32_t w, float* __restrict__ r, int64_t s, int64_t e, double& acc0,
-                                          double& acc1) {
-    int32_t lo = 0, hi = L;   // first layer ending after s (uniform binary search)
-    while (lo < hi) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (offsets[mid + 1] <= s) lo = mid + 1;
-        else hi = mid;
-    }
+                                          double& acc1, int32_t lo0) {
+    int32_t lo = lo0;   // a layer at or before the one holding s
+    while (offsets[lo + 1] <= s) ++lo;
     for (int32_t l = lo; l < L && offsets[l] < e; ++l) {
         const int64_t off = offsets[l], end = offsets[l + 1];
         const int64_t slot = (int64_t)w * L + l;
@@ -173,20 +169,31 @@ __device__ __forceinline__ void norm_walk(const HistArgs& h, const int64_t* __re
     }
 }
 
-// One workgroup per (worker w = blockIdx.y, chunk c = blockIdx.x).
-// STORE: a storing step.  FLUSH: write the residual after this step instead
-// of keys: zero on the chunks set in sel, and, unless this step stored (then
-// R already holds a), a elsewhere.
+// One workgroup per (worker w = blockIdx.y, part q of chunk c: blockIdx.x =
+// c * S + q), the part being elements [c*C + q*kNormPart, +kNormPart) of the
+// chunk (the whole chunk when S == 1).  With parts, consecutive workgroups
+// take consecutive parts, so the resident ones stream one contiguous window
+// of the residual and the gradients.  STORE: a storing step.  FLUSH: write the
+// residual after this step instead of keys: zero on the chunks set in sel,
+// and, unless this step stored (then R already holds a), a elsewhere.  The
+// part's binary64 sum of squares goes to keys[w][c] (S == 1) or to
+// part_keys[w][c][q], added per chunk by k_key_parts.
 template <bool FP16, int AGE, bool STORE, bool FLUSH>
 __global__ __launch_bounds__(kNormThreads) void k_norm_hist(HistArgs h, const int64_t* __restrict__ offsets,
                                                             int32_t L, float* __restrict__ resid, int64_t ld,
-                                                            int64_t P, int64_t C, int32_t mw,
-                                                            double* __restrict__ keys,
-                                                            const uint32_t* __restrict__ sel, int32_t stored) {
+                                                            int64_t P, int64_t C, int32_t mw, int64_t n_c,
+                                                            int32_t S, double* __restrict__ keys,
+                                                            double* __restrict__ part_keys,
+                                                            const uint32_t* __restrict__ sel, int32_t stored,
+                                                            const uint32_t* __restrict__ tile_layer,
+                                                            int64_t tile_elems) {
     const int32_t w = (int32_t)blockIdx.y;
-    const int32_t c = (int32_t)blockIdx.x;
-    const int64_t s = (int64_t)c * C;
-    const int64_t e = s + C < P ? s + C : P;
+    const int32_t c = (int32_t)(blockIdx.x / (uint32_t)S);
+    const int32_t q = (int32_t)(blockIdx.x - (uint32_t)c * (uint32_t)S);
+    const int64_t cs = (int64_t)c * C;
+    const int64_t ce = cs + C < P ? cs + C : P;
+    const int64_t s = S == 1 ? cs : cs + (int64_t)q * kNormPart;
+    const int64_t e = S == 1 ? ce : (s + kNormPart < ce ? s + kNormPart : ce);   // e <= s: an empty part
     float* __restrict__ r = resid + (int64_t)w * ld;
     if (FLUSH) {
         if (mask_bit(sel, w, mw, c)) {
@@ -195,29 +202,37 @@ __global__ __launch_bounds__(kNormThreads) void k_norm_hist(HistArgs h, const in
         }
         if (stored) return;
     }
-    // the residual's case: sent j steps back (n = j, base +0), else n = age on R
+    // the residual's case: sent j steps back (n = j, base +0), else n = age on R;
+    // the mask words and the tile's layer are requested together
+    uint32_t mwd[AGE + 1];
+#pragma unroll
+    for (int j = 0; j <= AGE; ++j)
+        mwd[j] = (j <= h.age && h.masks[j] != nullptr) ? h.masks[j][(int64_t)w * mw + (c >> 5)] : 0u;
+    const int32_t lo0 = s < e ? (int32_t)(tile_layer[s / tile_elems] & 0x7fffffffu) : 0;
     int32_t n = h.age;
     bool zero = false;
 #pragma unroll
     for (int j = 0; j <= AGE; ++j)
-        if (!zero && j <= h.age && h.masks[j] != nullptr && mask_bit(h.masks[j], w, mw, c)) {
+        if (!zero && ((mwd[j] >> (c & 31)) & 1u)) {
             n = j;
             zero = true;
         }
     constexpr bool ST = STORE || FLUSH;
     double acc0 = 0.0, acc1 = 0.0;
-    if (zero) {
-        if (n == 0) norm_walk<FP16, 0, false, ST>(h, offsets, L, w, r, s, e, acc0, acc1);
+    if (s >= e) {
+        // an empty part of the last chunk: it adds +0 to the chunk's key
+    } else if (zero) {
+        if (n == 0) norm_walk<FP16, 0, false, ST>(h, offsets, L, w, r, s, e, acc0, acc1, lo0);
         if constexpr (AGE >= 1)
-            if (n == 1) norm_walk<FP16, 1, false, ST>(h, offsets, L, w, r, s, e, acc0, acc1);
+            if (n == 1) norm_walk<FP16, 1, false, ST>(h, offsets, L, w, r, s, e, acc0, acc1, lo0);
         if constexpr (AGE >= 2)
-            if (n == 2) norm_walk<FP16, 2, false, ST>(h, offsets, L, w, r, s, e, acc0, acc1);
+            if (n == 2) norm_walk<FP16, 2, false, ST>(h, offsets, L, w, r, s, e, acc0, acc1, lo0);
     } else {
-        if (n == 0) norm_walk<FP16, 0, true, ST>(h, offsets, L, w, r, s, e, acc0, acc1);
+        if (n == 0) norm_walk<FP16, 0, true, ST>(h, offsets, L, w, r, s, e, acc0, acc1, lo0);
         if constexpr (AGE >= 1)
-            if (n == 1) norm_walk<FP16, 1, true, ST>(h, offsets, L, w, r, s, e, acc0, acc1);
+            if (n == 1) norm_walk<FP16, 1, true, ST>(h, offsets, L, w, r, s, e, acc0, acc1, lo0);
         if constexpr (AGE >= 2)
-            if (n == 2) norm_walk<FP16, 2, true, ST>(h, offsets, L, w, r, s, e, acc0, acc1);
+            if (n == 2) norm_walk<FP16, 2, true, ST>(h, offsets, L, w, r, s, e, acc0, acc1, lo0);
     }
     if (FLUSH) return;
     const double t = wave_sum(acc0 + acc1);
@@ -228,22 +243,44 @@ __global__ __launch_bounds__(kNormThreads) void k_norm_hist(HistArgs h, const in
     if (threadIdx.x == 0) {
         double k = part[0];
 #pragma unroll
-        for (int q = 1; q < kNormThreads / 64; ++q) k += part[q];
-        keys[(int64_t)w * gridDim.x + c] = k;
+        for (int j = 1; j < kNormThreads / 64; ++j) k += part[j];
+        if (S == 1) keys[(int64_t)w * n_c + c] = k;
+        else part_keys[((int64_t)w * n_c + c) * S + q] = k;
     }
+}
+
+// keys[i] = the S partial sums of key i added in part order (binary64).
+__global__ __launch_bounds__(256) void k_key_parts(const double* __restrict__ part_keys, int32_t S, int64_t n,
+                                                   double* __restrict__ keys) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const double* pk = part_keys + i * S;
+    double k = pk[0];
+    for (int32_t j = 1; j < S; ++j) k += pk[j];
+    keys[i] = k;
 }
 
 template <bool FP16, int AGE>
 hipError_t norm_launch(const Plan& p, const HistArgs& h, bool store, bool flush, float* resid, double* keys,
                        const uint32_t* sel, bool stored, hipStream_t s) {
-    const dim3 grid((unsigned)p.n_c, (unsigned)p.W);
+    // Storing passes run on 2048-element parts (their mixed read/write stream
+    // measured faster as one contiguous window); read-only passes and the
+    // flush sweep whole chunks, which measured faster for reads.
+    const int32_t S = (store && !flush) ? p.key_parts : 1;
+    const dim3 grid((unsigned)(p.n_c * S), (unsigned)p.W);
 #define GA_NH(ST, FL)                                                                                      \
     hipLaunchKernelGGL((k_norm_hist<FP16, AGE, ST, FL>), grid, dim3(kNormThreads), 0, s, h, p.d_offsets, p.L, \
-                       resid, p.ld, p.P, p.C, p.mw, keys, sel, stored ? 1 : 0)
+                       resid, p.ld, p.P, p.C, p.mw, p.n_c, S, keys, p.d_part_keys, sel, stored ? 1 : 0, p.d_tile_layer,     \
+                       p.tile_elems)
     if (flush) GA_NH(false, true);
     else if (store) GA_NH(true, false);
     else GA_NH(false, false);
 #undef GA_NH
+    if (!flush && S > 1) {
+        const int64_t n = (int64_t)p.W * p.n_c;
+        hipLaunchKernelGGL(k_key_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.d_part_keys, S, n,
+                           keys);
+    }
     return hipGetLastError();
 }
 

@@ -9,6 +9,14 @@
 
 namespace ga {
 
+// The storing layer-table chunk-norm pass splits a chunk longer than this
+// many elements into parts of this size, one workgroup each, so that the
+// resident workgroups stream one contiguous window of the residual instead of
+// one sweep per chunk (measured faster for its mixed read/write traffic, and
+// slower for read-only passes, which keep one workgroup per chunk); the
+// parts' binary64 sums are added per chunk afterwards.
+constexpr int64_t kNormPart = 2048;
+
 struct Plan {
     int32_t W, L, dtype, k, mw;
     int64_t P, ld, C, n_c;
@@ -26,6 +34,12 @@ struct Plan {
     // Same allocation as d_tile_layer (its second half).
     uint32_t* d_tile_order;
     int64_t tile_elems, n_tiles;
+    // Parts per chunk of the storing layer-table chunk-norm pass
+    // (ceil(C / kNormPart), 1 for C <= kNormPart), and the plan's workspace of
+    // their partial sums, [W][n_c][key_parts] binary64 (nullptr when
+    // key_parts == 1).
+    int32_t key_parts;
+    double* d_part_keys;
 };
 
 // ---- ABI error reporting (defined in abi.hip) ---------------------------

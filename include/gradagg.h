@@ -32,10 +32,15 @@
  *
  * Ownership.  The caller allocates and owns every buffer passed in; all
  * pointers named d_* are device pointers on the plan's device.  A plan owns
- * only a small device table of layer offsets, allocated in ga_plan_create and
- * freed in ga_plan_destroy.  Every call is asynchronous on `stream`, allocates
- * nothing and does not synchronize.  A plan is immutable after creation and may
- * be shared by threads and streams.  Host arrays are read before return.
+ * small device tables (layer offsets, the layer of each wavefront tile) and,
+ * for a chunk longer than 2048 elements, a workspace of W * n_c * ceil(C/2048)
+ * binary64 partial chunk sums, all allocated in ga_plan_create and freed in
+ * ga_plan_destroy.  Every call is asynchronous on `stream`, allocates nothing
+ * and does not synchronize.  A plan may be shared by threads and streams, with
+ * one exception: the storing norm passes of ga_chunk_norm_layers and
+ * ga_chunk_norm_deferred (store != 0) write the plan's workspace, so two of
+ * them on one plan must not run at the same time (issue them on one stream or
+ * order them with events).  Host arrays are read before return.
  *
  * Errors.  Arguments are validated on the host before any launch: a bad size,
  * a NULL pointer or a keep ratio outside [0,1] gives GA_ERR_INVALID; a device
@@ -63,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GA_ABI_VERSION 2
+#define GA_ABI_VERSION 3
 #define GA_MAX_WORKERS 1024
 #define GA_MAX_CHUNKS 65536
 /* Most elements per worker (P) of a plan or an SGD call: every 1-D grid of
@@ -217,7 +222,9 @@ ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_resi
  * ga_chunk_norm with zero-copy fusion: the gradient is read straight from the
  * workers' per-layer tensors (d_layer_ptrs as in ga_bucket_pack); a chunk that
  * spans several layers is assembled from each of them.  d_residual, the keys
- * and the lazy-zero mode are as in ga_chunk_norm.
+ * and the lazy-zero mode are as in ga_chunk_norm.  Uses the plan's workspace
+ * when C > 2048: not concurrently with another storing norm pass on the same
+ * plan.
  */
 ga_status ga_chunk_norm_layers(const ga_plan* plan, const uint64_t* d_layer_ptrs, float* d_residual,
                                const uint32_t* d_prev_mask, double* d_keys, hipStream_t stream);
@@ -327,7 +334,9 @@ typedef struct {
 /*
  * The norm pass of a deferred step: for every worker and chunk, a_t = g_t +
  * r_{t-1} (r_{t-1} re-formed as above), its key as in ga_chunk_norm, and with
- * store != 0, d_residual <- a_t on every chunk.  d_layer_ptrs: this step's
+ * store != 0, d_residual <- a_t on every chunk.  With store != 0 and C > 2048
+ * it uses the plan's workspace: not concurrently with another storing norm
+ * pass on the same plan.  d_layer_ptrs: this step's
  * layer table.  Errors: GA_ERR_INVALID (NULL argument, dense-only plan, age
  * outside [0, GA_MAX_AGE], a missing earlier table, an earlier table pointer
  * equal to this step's or to another earlier one: the tensors of different

@@ -114,7 +114,10 @@ def run_history(ga, wl, schedule, mis="aligned", steps=6, hook=None, strict=Fals
 
 CONFIGS = [(1, [3000, 7, 2000], 256), (3, workloads.WORKLOADS["tiny"].numels, 512),
            (16, [8, 1, 5000, 7, 4096, 333, 64], 256), (33, [20000, 37, 4003], 1024),
-           (128, [2048, 16, 4099, 520], 256), (300, [3000, 17, 1000], 512)]
+           (128, [2048, 16, 4099, 520], 256), (300, [3000, 17, 1000], 512),
+           # chunks longer than one 2048-element norm part: three parts (the
+           # last of 256), the last chunk 1197 long (two parts empty); four
+           (7, [5000, 3, 9000, 250], 4352), (40, [20000, 37, 4003], 8192)]
 
 
 @pytest.mark.parametrize("period", [1, 2, 3])

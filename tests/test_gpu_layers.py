@@ -48,7 +48,10 @@ def test_tree_reduce_layers(ga, fp16, W, numels, mis):
 
 @pytest.mark.parametrize("fp16", [False, True])
 @pytest.mark.parametrize("C,numels", [(64, workloads.WORKLOADS["tiny"].numels), (256, [1000, 17, 3000, 8, 40]),
-                                      (8, [5, 11, 100])])
+                                      (8, [5, 11, 100]),
+                                      # chunks split into 2048-element norm parts: the last
+                                      # chunk's second part empty; a ragged third part
+                                      (2304, [5000, 3, 9000, 250]), (6144, [20000, 37, 4003])])
 @pytest.mark.parametrize("mis", list(MIS))
 @pytest.mark.parametrize("lazy", [False, True])
 def test_chunk_norm_layers(ga, fp16, C, numels, mis, lazy):
