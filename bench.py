@@ -952,24 +952,39 @@ def selection_stats(plan, prev, cur, P):
             "n_chunks": int(n_c)}
 
 
+def code_digest(texts):
+    """SHA-256 of C/C++ sources with comments, trailing blanks and empty lines
+    removed: a change to the code changes it, a change to a comment does not."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for t in texts:
+        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", "", t)
+        lines = [l.rstrip() for l in t.splitlines()]
+        h.update("\n".join(l for l in lines if l).encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def measured_traffic(path, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
-    or None when there is none or the kernel's sources changed since it was taken."""
+    or None when there is none or the code of the kernel's sources changed since it
+    was taken (comments aside)."""
     if not os.path.exists(path):
         return None
-    import hashlib
     with open(path) as f:
         rec = json.load(f).get(kernel)
     if not rec:
         return None
-    h = hashlib.sha256()
+    texts = []
     for src in rec["sources"]:
         path_src = os.path.join(ROOT, src)
         if not os.path.exists(path_src):
             return None
-        with open(path_src, "rb") as f:
-            h.update(f.read())
-    return rec if h.hexdigest() == rec["sources_sha256"] else None
+        with open(path_src) as f:
+            texts.append(f.read())
+    return rec if code_digest(texts) == rec.get("code_sha256") else None
 
 
 def cpu_baseline(wl, plan, host_bucket, w_init, thr, min_s=10.0, max_steps=5):

@@ -17,10 +17,13 @@
 // These are the recurrence's own operations in its own order, so every a is
 // the one the plain recurrence computes, bit for bit.
 //
-//   k_norm_hist    one workgroup per (worker, chunk): forms a, its key
-//                  (binary64 sum of squares) and, on a storing step, writes a
-//                  into R; as the flush, writes the residual itself (zero on
-//                  the chunks sent this step).
+//   k_norm_hist    forms a, its key (binary64 sum of squares) and, on a
+//                  storing step, writes a into R; as the flush, writes the
+//                  residual itself (zero on the chunks sent this step).  One
+//                  workgroup per (worker, chunk), except on storing steps
+//                  with chunks longer than 2048 elements: one per (worker,
+//                  2048-element part), the parts' sums then added per chunk
+//                  in part order by k_key_parts.
 //   k_gather_hist  one wavefront per 256 or 512 elements of one chunk: the fixed
 //                  binary tree over the workers' sent values (absent workers
 //                  are +0), the mean and the fused momentum-SGD update, on a

@@ -52,20 +52,22 @@ def test_selection_stats_brute_force():
     assert bench.selection_stats(plan, None, _mask(cur, W, n_c), P)["pairs_newly_sent"] == len(cur)
 
 
-def test_traffic_needs_the_profiled_sources(tmp_path):
-    """A counter record is returned while its sources hash as recorded, and not
-    once one of them changes or is missing."""
-    import hashlib
+def test_traffic_needs_the_profiled_code(tmp_path):
+    """A counter record is returned while the code of its sources is the code
+    it was measured on (comments and blank lines aside), and not once the code
+    changes or a source is missing."""
     src = tmp_path / "k.hip"
-    src.write_text("kernel v1\n")
+    src.write_text("int f(int x) {\n    return x + 1;  // v1\n}\n")
     rel = os.path.relpath(str(src), bench.ROOT)
-    rec = {"k_x": {"bytes_per_launch": 123, "sources": [rel],
-                   "sources_sha256": hashlib.sha256(b"kernel v1\n").hexdigest(), "summary": "s.md"}}
+    rec = {"k_x": {"bytes_per_launch": 123, "sources": [rel], "code_sha256": bench.code_digest([src.read_text()]),
+                   "summary": "s.md"}}
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(rec))
     assert bench.measured_traffic(str(path), "k_x")["bytes_per_launch"] == 123
     assert bench.measured_traffic(str(path), "k_other") is None
-    src.write_text("kernel v2\n")
+    src.write_text("/* the kernel,\n   described */\nint f(int x) {\n\n    return x + 1;  // v2\n}\n")
+    assert bench.measured_traffic(str(path), "k_x")["bytes_per_launch"] == 123
+    src.write_text("int f(int x) {\n    return x + 2;  // v1\n}\n")
     assert bench.measured_traffic(str(path), "k_x") is None
     src.unlink()
     assert bench.measured_traffic(str(path), "k_x") is None
