@@ -43,7 +43,11 @@ def draw(seed):
         numels.append(n)
     fp16 = bool(rng.random() < 0.6)
     sparse = bool(rng.random() < 0.5)
-    chunk = (256 * int(rng.integers(1, 4)) if rng.random() < 0.4 else 8 * int(rng.integers(1, 65))) if sparse else 0
+    u = rng.random()
+    # a multiple of 256 (the deferred form applies), one longer than a 2048-element
+    # norm part (the storing pass splits it), or any multiple of 8
+    chunk = ((256 * int(rng.integers(1, 4)) if u < 0.4 else 256 * int(rng.integers(9, 33)) if u < 0.55
+              else 8 * int(rng.integers(1, 65))) if sparse else 0)
     rho = float(rng.choice([0.0, 0.05, 0.1, 0.25, 0.5, 1.0, rng.random()])) if sparse else 0.0
     lazy = bool(rng.random() < 0.5)
     # deferred residual where it applies (C a multiple of 256)
