@@ -279,8 +279,8 @@ hipError_t norm_launch(const Plan& p, const HistArgs& h, bool store, bool flush,
     const dim3 grid((unsigned)(p.n_c * S), (unsigned)p.W);
 #define GA_NH(ST, FL)                                                                                      \
     hipLaunchKernelGGL((k_norm_hist<FP16, AGE, ST, FL>), grid, dim3(kNormThreads), 0, s, h, p.d_offsets, p.L, \
-                       resid, p.ld, p.P, p.C, p.mw, p.n_c, S, keys, p.d_part_keys, sel, stored ? 1 : 0, p.d_tile_layer,     \
-                       p.tile_elems)
+                       resid, p.ld, p.P, p.C, p.mw, p.n_c, S, keys, p.d_part_keys, sel, stored ? 1 : 0,        \
+                       p.d_tile_layer, p.tile_elems)
     if (flush) GA_NH(false, true);
     else if (store) GA_NH(true, false);
     else GA_NH(false, false);
