@@ -953,16 +953,17 @@ def selection_stats(plan, prev, cur, P):
 
 
 def code_digest(texts):
-    """SHA-256 of C/C++ sources with comments, trailing blanks and empty lines
-    removed: a change to the code changes it, a change to a comment does not."""
+    """SHA-256 of C/C++ sources with comments and all whitespace removed: a
+    change to the code changes it, a change to a comment or to the layout of
+    the lines does not."""
     import hashlib
     import re
     h = hashlib.sha256()
     for t in texts:
-        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
-        t = re.sub(r"//[^\n]*", "", t)
-        lines = [l.rstrip() for l in t.splitlines()]
-        h.update("\n".join(l for l in lines if l).encode())
+        t = t.replace("\\\n", "")   # continued lines spliced first, as C does
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(re.sub(r"\s+", "", t).encode())
         h.update(b"\0")
     return h.hexdigest()
 
