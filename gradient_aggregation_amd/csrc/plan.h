@@ -54,6 +54,9 @@ hipError_t launch_tree_scaled(const Plan& p, const void* bucket, float scale, fl
                               float* w, float* v, hipStream_t s);
 hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid,
                              const uint32_t* prev_mask, double* keys, hipStream_t s);
+// After a part-split storing norm pass: keys[w][c] = the chunk's key_parts
+// partial sums in the plan's workspace, added in part order.
+hipError_t launch_key_parts(const Plan& p, double* keys, hipStream_t s);
 // The deferred-residual form (history.hip).  layers[0] is this step's layer
 // table and layers[j] that of step t-j (j <= age); masks[j] the selection of
 // step t-1-j (j <= age), or nullptr.

@@ -37,10 +37,11 @@
  * binary64 partial chunk sums, all allocated in ga_plan_create and freed in
  * ga_plan_destroy.  Every call is asynchronous on `stream`, allocates nothing
  * and does not synchronize.  A plan may be shared by threads and streams, with
- * one exception: the storing norm passes of ga_chunk_norm_layers and
- * ga_chunk_norm_deferred (store != 0) write the plan's workspace, so two of
- * them on one plan must not run at the same time (issue them on one stream or
- * order them with events).  Host arrays are read before return.
+ * one exception: the storing norm passes (ga_chunk_norm, ga_chunk_norm_topk,
+ * ga_chunk_norm_topk_static, ga_chunk_norm_layers, and ga_chunk_norm_deferred
+ * with store != 0) write the plan's workspace when C > 2048, so two of them on
+ * one plan must not run at the same time (issue them on one stream or order
+ * them with events).  Host arrays are read before return.
  *
  * Errors.  Arguments are validated on the host before any launch: a bad size,
  * a NULL pointer or a keep ratio outside [0,1] gives GA_ERR_INVALID; a device

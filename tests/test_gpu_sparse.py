@@ -85,7 +85,9 @@ TINY = workloads.TINY_LAYERS
 
 
 @pytest.mark.parametrize("fp16", [False, True])
-@pytest.mark.parametrize("C,rho", [(64, 0.25), (256, 0.1), (1024, 0.5), (8, 0.05)])
+@pytest.mark.parametrize("C,rho", [(64, 0.25), (256, 0.1), (1024, 0.5), (8, 0.05),
+                                   # chunks split into 2048-element norm parts (ragged, empty parts)
+                                   (4352, 0.3), (8192, 0.5)])
 @pytest.mark.parametrize("lazy", [False, True])
 def test_sparse_tiny(ga, fp16, C, rho, lazy):
     numels = [int(np.prod(s)) for s in TINY]

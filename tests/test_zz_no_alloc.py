@@ -88,6 +88,14 @@ def test_static_keys_two_calls_second_smaller(ga):
     run_both(ga, small, steps=3)
 
 
+def test_static_keys_long_chunks(ga):
+    """Chunks longer than 2048 elements: the norm pass sums 2048-element parts
+    in the plan's workspace, then adds them into the fixed key array."""
+    wl = workloads.custom(9, [20000, 37, 4003], True, sigma=1e-3, scale_mode="chunk", scale_log10=(-4.0, 0.0),
+                          chunk=4352, rho=0.3)
+    run_both(ga, wl, steps=3)
+
+
 def test_static_keys_limit(ga):
     """W * n_c beyond the fixed array is refused before any launch; at the
     limit it runs."""
