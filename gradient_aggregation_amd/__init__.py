@@ -25,7 +25,7 @@ ORDERS = {"tree": 0, "server": 1, "ring": 2}
 MAX_WORKERS = 1024
 MAX_CHUNKS = 65536
 MAX_ELEMENTS = 1 << 33
-STATIC_KEYS = 1 << 20
+STATIC_KEYS = 1 << 22
 
 
 class GAError(RuntimeError):
@@ -395,8 +395,9 @@ class Plan:
             _dev(sel_mask, torch.int32, self.W * self.mask_words, "sel_mask"), _stream_ptr()))
 
     def chunk_norm_topk_static(self, bucket, resid, sel_idx, sel_mask, prev_mask=None) -> None:
-        """chunk_norm_topk with the keys in the library's fixed array (no
-        allocation; concurrent calls on one device race)."""
+        """chunk_norm_topk with the keys (and the partial sums of chunks longer
+        than 2048 elements) in the library's fixed array (no allocation;
+        concurrent calls on one device race)."""
         torch = _torch()
         _check(lib().ga_chunk_norm_topk_static(
             self._h, _dev(bucket, self.grad_dtype, self.W * self.ld, "bucket"),

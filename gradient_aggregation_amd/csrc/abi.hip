@@ -105,7 +105,7 @@ ga_status check_device(const ga::Plan* p) {
 }  // namespace
 
 namespace ga {
-// The fixed key array of ga_chunk_norm_topk_static (noalloc.hip): look up its
+// The fixed array of ga_chunk_norm_topk_static (noalloc.hip): look up its
 // address on `device` (which must be current) once; then static_keys(device)
 // returns it (nullptr before, or if the lookup failed).
 hipError_t static_keys_setup(int device);
@@ -214,7 +214,7 @@ ga_status ga_plan_create(int32_t W, int32_t n_layers, const int64_t* layer_numel
         delete p;
         return device_status(e, "plan device table");
     }
-    // the fixed key array of ga_chunk_norm_topk_static: its address on this
+    // the fixed array of ga_chunk_norm_topk_static: its address on this
     // device, looked up once per device (a failure shows as GA_ERR_DEVICE from
     // that call only)
     (void)ga::static_keys_setup(p->device);
@@ -407,8 +407,9 @@ ga_status ga_chunk_norm(const ga_plan* plan, const void* d_bucket, float* d_resi
         return fail(GA_ERR_ALIGN, "misaligned device buffer");
     ga_status st = check_device(p);
     if (st != GA_OK) return st;
-    return device_status(ga::launch_chunk_norm(*p, d_bucket, d_residual, d_prev_mask, d_keys, stream),
-                         "chunk_norm launch");
+    return device_status(
+        ga::launch_chunk_norm(*p, d_bucket, d_residual, d_prev_mask, d_keys, p->d_part_keys, stream),
+        "chunk_norm launch");
 }
 
 ga_status ga_chunk_topk(const ga_plan* plan, const double* d_keys, int32_t* d_sel_idx, uint32_t* d_sel_mask,
@@ -441,17 +442,22 @@ ga_status ga_chunk_norm_topk_static(const ga_plan* plan, const void* d_bucket, f
     const ga::Plan* p = as_plan(plan);
     if (p->C == 0) return fail(GA_ERR_INVALID, "plan has no chunk size (dense-only plan)");
     if (p->k > 0 && !d_sel_idx) return fail(GA_ERR_INVALID, "sel_idx is NULL with k > 0");
-    if ((int64_t)p->W * p->n_c > GA_STATIC_KEYS)
-        return fail(GA_ERR_UNSUPPORTED, "W * n_c = %lld keys exceed the %lld of the fixed array",
-                    (long long)p->W * p->n_c, (long long)GA_STATIC_KEYS);
+    // the keys, then (chunks longer than 2048 elements) the parts' partial sums
+    const int64_t n_keys = (int64_t)p->W * p->n_c;
+    const int64_t need = n_keys * (p->key_parts > 1 ? 1 + (int64_t)p->key_parts : 1);
+    if (need > GA_STATIC_KEYS)
+        return fail(GA_ERR_UNSUPPORTED, "%lld binary64 values (W * n_c = %lld keys, %d parts) exceed the %lld of "
+                    "the fixed array", (long long)need, (long long)n_keys, (int)p->key_parts,
+                    (long long)GA_STATIC_KEYS);
     if (!aligned16(d_bucket) || !aligned16(d_residual) || (d_prev_mask && ((uintptr_t)d_prev_mask & 3u)) ||
         ((uintptr_t)d_sel_mask & 3u) || (d_sel_idx && ((uintptr_t)d_sel_idx & 3u)))
         return fail(GA_ERR_ALIGN, "misaligned device buffer");
     ga_status st = check_device(p);
     if (st != GA_OK) return st;
     double* keys = ga::static_keys(p->device);
-    if (!keys) return fail(GA_ERR_DEVICE, "the fixed key array has no address on device %d", p->device);
-    st = device_status(ga::launch_chunk_norm(*p, d_bucket, d_residual, d_prev_mask, keys, stream),
+    if (!keys) return fail(GA_ERR_DEVICE, "the fixed array has no address on device %d", p->device);
+    double* part_keys = p->key_parts > 1 ? keys + n_keys : nullptr;
+    st = device_status(ga::launch_chunk_norm(*p, d_bucket, d_residual, d_prev_mask, keys, part_keys, stream),
                        "chunk_norm_topk_static launch");
     if (st != GA_OK) return st;
     return device_status(ga::launch_topk(*p, keys, d_sel_idx, d_sel_mask, stream), "chunk_norm_topk_static launch");

@@ -285,7 +285,7 @@ hipError_t norm_launch(const Plan& p, const HistArgs& h, bool store, bool flush,
     else if (store) GA_NH(true, false);
     else GA_NH(false, false);
 #undef GA_NH
-    if (!flush && S > 1) return launch_key_parts(p, keys, s);
+    if (!flush && S > 1) return launch_key_parts(p, p.d_part_keys, keys, s);
     return hipGetLastError();
 }
 
@@ -694,9 +694,9 @@ hipError_t gather_launch(const Plan& p, const HistArgs& h, const float* resid, c
 
 }  // namespace
 
-hipError_t launch_key_parts(const Plan& p, double* keys, hipStream_t s) {
+hipError_t launch_key_parts(const Plan& p, const double* part_keys, double* keys, hipStream_t s) {
     const int64_t n = (int64_t)p.W * p.n_c;
-    hipLaunchKernelGGL(k_key_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.d_part_keys, p.key_parts,
+    hipLaunchKernelGGL(k_key_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part_keys, p.key_parts,
                        n, keys);
     return hipGetLastError();
 }

@@ -1,9 +1,11 @@
-// The chunk keys of ga_chunk_norm_topk_static in a fixed device array, for
+// The workspace of ga_chunk_norm_topk_static in a fixed device array, for
 // callers that cannot allocate device memory.
 //
-// `scratch` is the library's own copy of the [W][n_c] binary64 keys that
-// ga_chunk_norm_topk takes as a caller buffer.  Each device the library runs
-// on holds one until the process ends.  In host code the array's name is not
+// `scratch` holds the [W][n_c] binary64 keys that ga_chunk_norm_topk takes as
+// a caller buffer and, for chunks longer than 2048 elements, right after them
+// the [W][n_c][parts] partial sums that ga_chunk_norm_topk keeps in the plan's
+// workspace.  Each device the library runs on holds one until the process
+// ends.  In host code the array's name is not
 // a device address: its address on a device is looked up once, with that
 // device current, at plan creation, and only that looked-up pointer is ever
 // passed to a kernel.

@@ -6,7 +6,7 @@
 // (worker, 2048-element part) for chunks longer than 2048 elements (the
 // resident workgroups then stream one contiguous window, measured faster for
 // this mixed read/write pass; the parts' sums are added per chunk afterwards,
-// in part order, by the plan's key-sum kernel).  Each thread
+// in part order, by the key-sum kernel).  Each thread
 // takes 8-element vectors (one 128-bit binary16 load of the gradient, two of
 // the binary32 residual), 4 vectors in flight; a = leaf + residual is written
 // back over the residual, and the chunk's key, the sum of a^2 in binary64
@@ -109,8 +109,8 @@ __device__ __forceinline__ void norm_segment(gptr<void> __restrict__ src, int64_
 
 // One workgroup per (worker w = blockIdx.y, part q of chunk c: blockIdx.x =
 // c * S + q, the whole chunk when S == 1); the gradient is row w of the flat
-// [W][ld] bucket.  The sum of squares goes to keys[w][c] (S == 1) or to the
-// plan's workspace part_keys[w][c][q].
+// [W][ld] bucket.  The sum of squares goes to keys[w][c] (S == 1) or to
+// part_keys[w][c][q].
 template <bool FP16, bool LAZY>
 __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(const void* __restrict__ bucket,
                                                              float* __restrict__ resid, int64_t ld, int64_t P,
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kNormThreads) void k_chunk_norm(const void* __restr
 }  // namespace
 
 hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid, const uint32_t* prev_mask,
-                             double* keys, hipStream_t s) {
+                             double* keys, double* part_keys, hipStream_t s) {
     // a 2-D grid: W * n_c workgroups would exceed the 32-bit work-item count
     // of a 1-D dispatch at the plan limits
     if (p.W == 0 || p.n_c == 0) return hipSuccess;
@@ -156,14 +156,14 @@ hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid, co
     const dim3 grid((unsigned)(p.n_c * S), (unsigned)p.W);
 #define GA_NORM_LAUNCH(F, Z)                                                                                 \
     hipLaunchKernelGGL((k_chunk_norm<F, Z>), grid, dim3(kNormThreads), 0, s, bucket, resid, p.ld, p.P, p.C, \
-                       prev_mask, p.mw, p.n_c, S, keys, p.d_part_keys)
+                       prev_mask, p.mw, p.n_c, S, keys, part_keys)
     const bool f16 = p.dtype == GA_FP16;
     if (f16 && prev_mask) GA_NORM_LAUNCH(true, true);
     else if (f16) GA_NORM_LAUNCH(true, false);
     else if (prev_mask) GA_NORM_LAUNCH(false, true);
     else GA_NORM_LAUNCH(false, false);
 #undef GA_NORM_LAUNCH
-    if (S > 1) return launch_key_parts(p, keys, s);
+    if (S > 1) return launch_key_parts(p, part_keys, keys, s);
     return hipGetLastError();
 }
 

@@ -52,11 +52,13 @@ hipError_t launch_tree(const Plan& p, const void* bucket, float* grad, const ga_
 // launch_tree with g = S * scale instead of S * fl32(1/W).
 hipError_t launch_tree_scaled(const Plan& p, const void* bucket, float scale, float* grad, const ga_sgd* sgd,
                               float* w, float* v, hipStream_t s);
+// part_keys: [W][n_c][key_parts] binary64 partial sums when key_parts > 1
+// (the plan's workspace, or the fixed array of the allocation-free call).
 hipError_t launch_chunk_norm(const Plan& p, const void* bucket, float* resid,
-                             const uint32_t* prev_mask, double* keys, hipStream_t s);
+                             const uint32_t* prev_mask, double* keys, double* part_keys, hipStream_t s);
 // After a part-split storing norm pass: keys[w][c] = the chunk's key_parts
-// partial sums in the plan's workspace, added in part order.
-hipError_t launch_key_parts(const Plan& p, double* keys, hipStream_t s);
+// partial sums in part_keys, added in part order.
+hipError_t launch_key_parts(const Plan& p, const double* part_keys, double* keys, hipStream_t s);
 // The deferred-residual form (history.hip).  layers[0] is this step's layer
 // table and layers[j] that of step t-j (j <= age); masks[j] the selection of
 // step t-1-j (j <= age), or nullptr.

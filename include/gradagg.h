@@ -38,10 +38,10 @@
  * ga_plan_destroy.  Every call is asynchronous on `stream`, allocates nothing
  * and does not synchronize.  A plan may be shared by threads and streams, with
  * one exception: the storing norm passes (ga_chunk_norm, ga_chunk_norm_topk,
- * ga_chunk_norm_topk_static, ga_chunk_norm_layers, and ga_chunk_norm_deferred
- * with store != 0) write the plan's workspace when C > 2048, so two of them on
- * one plan must not run at the same time (issue them on one stream or order
- * them with events).  Host arrays are read before return.
+ * ga_chunk_norm_layers, and ga_chunk_norm_deferred with store != 0) write the
+ * plan's workspace when C > 2048, so two of them on one plan must not run at
+ * the same time (issue them on one stream or order them with events).  Host
+ * arrays are read before return.
  *
  * Errors.  Arguments are validated on the host before any launch: a bad size,
  * a NULL pointer or a keep ratio outside [0,1] gives GA_ERR_INVALID; a device
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GA_ABI_VERSION 3
+#define GA_ABI_VERSION 4
 #define GA_MAX_WORKERS 1024
 #define GA_MAX_CHUNKS 65536
 /* Most elements per worker (P) of a plan or an SGD call: every 1-D grid of
@@ -250,20 +250,23 @@ ga_status ga_chunk_norm_topk(const ga_plan* plan, const void* d_bucket, float* d
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * operation as ga_chunk_norm_topk, with the [W][n_c] binary64 keys held in a
- * fixed array inside the library instead of a caller buffer.  The array holds
- * GA_STATIC_KEYS keys (8 MiB) on every device the library runs on, until the
- * process ends; its address on a device is looked up when a plan is created
- * there.  The call allocates nothing and calls no allocating routine.
- * Every call on one device uses the same array, so calls that overlap on one
- * device (other streams, other threads) race; each call overwrites every key
- * it reads, so nothing needs clearing between calls.  Results equal
- * ga_chunk_norm_topk's bit for bit.
+ * operation as ga_chunk_norm_topk, with its whole workspace in a fixed array
+ * inside the library: the [W][n_c] binary64 keys (a caller buffer there) and,
+ * for C > 2048, the W * n_c * ceil(C/2048) binary64 partial sums (the plan's
+ * workspace there), so the plan's workspace is not used.  The array holds
+ * GA_STATIC_KEYS binary64 values (32 MiB) on every device the library runs
+ * on, until the process ends; its address on a device is looked up when a
+ * plan is created there.  The call allocates nothing and calls no allocating
+ * routine.  Every call on one device uses the same array, so calls that
+ * overlap on one device (other streams, other threads) race; each call
+ * overwrites every value it reads, so nothing needs clearing between calls.
+ * Results equal ga_chunk_norm_topk's bit for bit.
  * Errors: those of ga_chunk_norm_topk (d_keys aside); GA_ERR_UNSUPPORTED when
- * W * n_c > GA_STATIC_KEYS; GA_ERR_DEVICE when the array's address could not
- * be looked up on the plan's device.
+ * W * n_c > GA_STATIC_KEYS, or, for C > 2048, W * n_c * (1 + ceil(C/2048)) >
+ * GA_STATIC_KEYS; GA_ERR_DEVICE when the array's address could not be looked
+ * up on the plan's device.
  */
-#define GA_STATIC_KEYS ((int64_t)1 << 20)
+#define GA_STATIC_KEYS ((int64_t)1 << 22)
 ga_status ga_chunk_norm_topk_static(const ga_plan* plan, const void* d_bucket, float* d_residual,
                                     const uint32_t* d_prev_mask, int32_t* d_sel_idx, uint32_t* d_sel_mask,
                                     hipStream_t stream);

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(ga):
     lib = ctypes.CDLL(ga.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
-    assert ga.lib().ga_abi_version() == 3
+    assert ga.lib().ga_abi_version() == 4
 
 
 def test_status_strings(ga):

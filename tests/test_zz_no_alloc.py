@@ -1,7 +1,8 @@
 """ga_chunk_norm_topk_static, the entry point that allocates nothing (its
-binary64 keys live in a fixed array inside the library), called through the
-C ABI and checked against ga_chunk_norm_topk with a caller key buffer, bit for
-bit: on two calls in a row, the second with a smaller plan (so the array holds
+binary64 keys, and the partial sums of chunks longer than 2048 elements, live
+in a fixed array inside the library), called through the C ABI and checked
+against ga_chunk_norm_topk with a caller key buffer, bit for bit: on two calls
+in a row, the second with a smaller plan (so the array holds
 the first call's keys when it starts), in plain and lazy-zero mode, and
 against the oracle.  Oversized plans are refused before any launch."""
 import ctypes
@@ -90,29 +91,48 @@ def test_static_keys_two_calls_second_smaller(ga):
 
 def test_static_keys_long_chunks(ga):
     """Chunks longer than 2048 elements: the norm pass sums 2048-element parts
-    in the plan's workspace, then adds them into the fixed key array."""
+    into the fixed array (after the keys), then adds them into the keys; the
+    caller-buffer call does the same in the plan's workspace."""
     wl = workloads.custom(9, [20000, 37, 4003], True, sigma=1e-3, scale_mode="chunk", scale_log10=(-4.0, 0.0),
                           chunk=4352, rho=0.3)
     run_both(ga, wl, steps=3)
 
 
-def test_static_keys_limit(ga):
-    """W * n_c beyond the fixed array is refused before any launch; at the
-    limit it runs."""
+def _limit_case(ga, W, chunk, n_c, status):
     L = ga.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    W = 1024
-    n_c = ga.STATIC_KEYS // W
-    for chunks, status in ((n_c + 1, ga.GA_ERR_UNSUPPORTED), (n_c, ga.GA_OK)):
-        plan = ga.Plan(W, [8 * chunks], True, chunk=8, keep_ratio=0.01)
+    plan = ga.Plan(W, [chunk * n_c], True, chunk=chunk, keep_ratio=0.01)
+    assert plan.n_chunks == n_c
+    print("[no-alloc limit] W=%d C=%d n_c=%d expect %d" % (W, chunk, n_c, status), flush=True)
+    if status == ga.GA_OK:
         bd = torch.zeros((W, plan.ld), dtype=torch.float16, device="cuda")
         rd = plan.empty_residual()
-        idx = torch.zeros((W, plan.k), dtype=torch.int32, device="cuda")
-        mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
-        st = L.ga_chunk_norm_topk_static(plan._h, _ptr(bd), _ptr(rd), None, _ptr(idx), _ptr(mask), stream)
-        assert st == status, (chunks, L.ga_last_error())
-        torch.cuda.synchronize()
-        if status == ga.GA_OK:
-            # all-zero keys: the k lowest chunk indices in every row
-            assert np.array_equal(host(idx), np.tile(np.arange(plan.k, dtype=np.int32), (W, 1)))
-        plan.close()
+    else:
+        # refused before any launch: nothing is read through these pointers
+        bd = torch.zeros(8, dtype=torch.float16, device="cuda")
+        rd = torch.zeros(8, dtype=torch.float32, device="cuda")
+    idx = torch.zeros((W, plan.k), dtype=torch.int32, device="cuda")
+    mask = torch.zeros((W, plan.mask_words), dtype=torch.int32, device="cuda")
+    st = L.ga_chunk_norm_topk_static(plan._h, _ptr(bd), _ptr(rd), None, _ptr(idx), _ptr(mask), stream)
+    assert st == status, (W, chunk, n_c, L.ga_last_error())
+    torch.cuda.synchronize()
+    if status == ga.GA_OK:
+        # all-zero keys: the k lowest chunk indices in every row
+        assert np.array_equal(host(idx), np.tile(np.arange(plan.k, dtype=np.int32), (W, 1)))
+    del bd, rd
+    plan.close()
+
+
+def test_static_keys_limit(ga):
+    """A workspace beyond the fixed array is refused before any launch; at the
+    limit it runs: W * n_c keys for chunks of at most 2048 elements,
+    W * n_c * (1 + parts) values for longer ones (here 2 parts of a
+    2056-element chunk: the partial sums end 1024 values short of the array's
+    end)."""
+    W = 1024
+    n_c = ga.STATIC_KEYS // W
+    _limit_case(ga, W, 8, n_c + 1, ga.GA_ERR_UNSUPPORTED)
+    _limit_case(ga, W, 8, n_c, ga.GA_OK)
+    n_c = ga.STATIC_KEYS // (W * 3)
+    _limit_case(ga, W, 2056, n_c + 1, ga.GA_ERR_UNSUPPORTED)
+    _limit_case(ga, W, 2056, n_c, ga.GA_OK)
