@@ -543,7 +543,8 @@ def main():
         del step, holder
         torch.cuda.empty_cache()
     if sparse and args.extras:
-        # the same workload under the survey's step protocol, and the lazy-zero
+        # the same workload under its own timing protocol (3 steps from a zero
+        # residual, repeated with a reset), and the lazy-zero
         # sequence of the boundary's calls, on the same resident batches
         result["protocol"] = {"deferred_depth%d" % args.depth if deferred else "lazy":
                               sparse_protocol(plan, wl, sources, w_init, "deferred" if deferred else "lazy",
